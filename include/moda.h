@@ -1,0 +1,144 @@
+/*
+ * libmoda -- Mixture-of-Depths Attention (MoDA) on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every entry point takes plain pointers and sizes; no C++ types or
+ * exceptions cross it.
+ *
+ * The operator.  For batch b, query head h (KV head kv = h / G with
+ * G = Hq / Hk), token t, with s = scale:
+ *
+ *   O[b,h,t] = softmax( s * Q[b,h,t] . [K[b,kv,0..t] || Kd[b,kv,t*L .. t*L+L-1]]^T )
+ *              . [V[b,kv,0..t] || Vd[b,kv,t*L .. t*L+L-1]]
+ *
+ * one softmax over the causal sequence keys of the current layer and the
+ * token's own L depth keys ("Mixture-of-Depths Attention", arXiv 2603.15619,
+ * paper summary, section 3.4 "Mixture-of-Depths Attention (MoDA): The Unified
+ * Operator": the MoDA equation, its sequence causal mask and its depth
+ * matching mask).  G adjacent query heads share one KV head ("moda-attention
+ * 0.1.0" PyPI page, "Key Design Choices", GQA bullet).  Depth rows are
+ * token-major: row t*L + l holds token t's slot l, so a token's depth keys are
+ * contiguous (paper summary, "Hardware-Efficient Implementation",
+ * "Flash-compatible depth-KV layout").  With L = 0 the operator is plain causal
+ * attention (same section, paragraph on the depth KV at different layers).
+ *
+ * Layouts (all row-major, contiguous, element type `dtype`):
+ *   Q, O, dQ, dO        [B, Hq, T, d]
+ *   K, V, dK, dV        [B, Hk, T, d]
+ *   Kd, Vd, dKd, dVd    [B, Hk, T*L, d]
+ *   lse                 [B, Hq, T]  float32 always
+ * (shapes of the PyPI page's "Using the Kernel Directly").
+ *
+ * Ownership and execution.  All tensors are device memory owned by the
+ * caller.  The library never allocates, frees or synchronises device memory;
+ * each call validates its arguments on the host, enqueues its kernels on
+ * `stream` (a hipStream_t; NULL means the null stream) and returns.  Device
+ * faults surface at the caller's next synchronisation.  Outputs must not alias
+ * inputs or each other.  Pointers must be 16-byte aligned.
+ *
+ * Errors.  Every argument check runs before anything is launched; on a
+ * non-OK status nothing was enqueued and outputs are untouched.
+ * moda_last_error() then returns a thread-local message naming the problem.
+ */
+#ifndef MODA_H
+#define MODA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MODA_OK = 0,
+    MODA_ERR_INVALID_ARGUMENT = 1, /* bad shape, pointer, alignment, scale or workspace */
+    MODA_ERR_UNSUPPORTED = 2,      /* valid request outside what this build implements */
+    MODA_ERR_HIP = 3               /* the HIP runtime reported an error; see moda_last_error */
+} moda_status_t;
+
+typedef enum {
+    MODA_BF16 = 0, /* bfloat16 storage, fp32 accumulation, MFMA contractions */
+    MODA_F32 = 1   /* fp32 storage and arithmetic throughout */
+} moda_dtype_t;
+
+/* Largest number of depth entries per token this build accepts. */
+#define MODA_MAX_L 1024
+
+typedef struct {
+    int64_t B;      /* batch, >= 1 */
+    int64_t Hq;     /* query heads, >= 1, multiple of Hk */
+    int64_t Hk;     /* KV heads, >= 1; G = Hq / Hk must divide 32 */
+    int64_t T;      /* tokens, >= 1 (any value; no multiple of a tile needed) */
+    int64_t d;      /* head dimension: 64 or 128 */
+    int64_t L;      /* depth entries per token, 0 .. MODA_MAX_L */
+    float scale;    /* score scale, finite and > 0 (normally 1/sqrt(d)) */
+    int32_t dtype;  /* moda_dtype_t */
+    int32_t chunk;  /* tokens per query chunk requested; 0 = library default.
+                       A tiling hint only: results do not depend on it beyond
+                       fp32 summation order. */
+    int32_t reserved; /* must be 0 */
+} moda_problem_t;
+
+/*
+ * Forward.  Writes O and the per-row log-sum-exp
+ *   lse[b,h,t] = ln( sum over the visible keys of exp(scale * q.k) )
+ * (natural log of the scaled scores; the backward pass reads it).
+ * Kd and Vd may be NULL when L == 0.
+ * Returns MODA_ERR_INVALID_ARGUMENT for: a NULL problem or pointer (other than
+ * Kd/Vd with L == 0), a pointer not 16-byte aligned, B, Hq, Hk or T < 1,
+ * Hq % Hk != 0, L < 0, a scale that is not finite or not > 0, reserved != 0,
+ * chunk < 0, or element counts that overflow int64.  Returns
+ * MODA_ERR_UNSUPPORTED for d not in {64, 128}, an unknown dtype, L > MODA_MAX_L
+ * or a GQA group size G that does not divide 32.
+ */
+moda_status_t moda_fwd(const moda_problem_t* p, const void* Q, const void* K, const void* V,
+                       const void* Kd, const void* Vd, void* O, float* lse, void* stream);
+
+/* Bytes of device workspace moda_bwd needs for problem p (0 for an invalid p). */
+size_t moda_bwd_workspace_bytes(const moda_problem_t* p);
+
+/*
+ * Backward: gradients of the forward's O with respect to Q, K, V, Kd and Vd,
+ * given the upstream gradient dO, the forward's O and lse (the derivative of
+ * the operator above; the pages time forward+backward, MoDA README "Kernel
+ * Efficiency" tables).  Every gradient is fully overwritten (dKd/dVd may be
+ * NULL when L == 0).  `workspace` is caller-owned device memory of at least
+ * moda_bwd_workspace_bytes(p) bytes, 256-byte aligned; it holds per-row
+ * scratch between the kernels of one call, so concurrent calls need separate
+ * workspaces.  Errors as for moda_fwd, plus MODA_ERR_INVALID_ARGUMENT when the
+ * workspace is NULL, misaligned or smaller than required.
+ */
+moda_status_t moda_bwd(const moda_problem_t* p, const void* Q, const void* K, const void* V,
+                       const void* Kd, const void* Vd, const void* O, const float* lse,
+                       const void* dO, void* dQ, void* dK, void* dV, void* dKd, void* dVd,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Depth-KV layout packer: layer-major depth entries layers[L, B, Hk, T, d]
+ * (entry l of every token contiguous, the natural per-layer layout whose
+ * stride between a token's layers defeats coalescing) to the token-major
+ * packed[B, Hk, T*L, d] that moda_fwd/moda_bwd read, packed row t*L + l =
+ * layers[l, b, kv, t] ("Mixture-of-Depths Attention" paper summary,
+ * "Hardware-Efficient Implementation": the natural layout paragraph and
+ * "Flash-compatible depth-KV layout").  A bitwise copy in p->dtype.  Requires
+ * L >= 1; other errors as for moda_fwd (d may be any value >= 1 with
+ * d * element size a multiple of 16 bytes).
+ */
+moda_status_t moda_pack_depth(const moda_problem_t* p, const void* layers, void* packed,
+                              void* stream);
+
+/* Static string naming a status code. */
+const char* moda_status_string(moda_status_t s);
+
+/* Thread-local detail of the last non-OK status returned on this thread. */
+const char* moda_last_error(void);
+
+/* Query-chunk tokens (folded query rows per workgroup / G) moda_fwd would use
+ * for p, or 0 if p is invalid or unsupported. */
+int32_t moda_fwd_chunk_tokens(const moda_problem_t* p);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MODA_H */

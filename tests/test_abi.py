@@ -1,0 +1,154 @@
+"""C-ABI tests that need no GPU: the library loads, exports every entry point
+declared in include/moda.h, and rejects invalid arguments on the host before
+any launch, with the documented status codes."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from transformer_attention_moda_amd import binding as mb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moda.h")
+
+# Fake device pointers: never dereferenced, because every call below fails validation.
+A = 0x10000          # 16-byte aligned
+MIS = 0x10008        # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported():
+    names = declared_functions()
+    assert set(names) == set(mb.EXPORTS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", mb.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for n in names:
+        assert n in exported, f"{n} not exported"
+    lib = mb.load()
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def prob(**kw):
+    base = dict(B=1, Hq=4, Hk=2, T=16, d=64, L=2, scale=0.125, dtype=mb.MODA_BF16, chunk=0)
+    base.update(kw)
+    return mb.problem(**base)
+
+
+def fwd_rc(p, ptrs=None):
+    q, k, v, kd, vd, o, lse = ptrs or (A,) * 7
+    lib = mb.load()
+    return lib.moda_fwd(ctypes.byref(p) if p is not None else None, q, k, v, kd, vd, o, lse,
+                        None)
+
+
+INVALID_PROBLEMS = [
+    dict(B=0), dict(Hq=0), dict(Hk=0), dict(T=0), dict(T=-3), dict(Hq=5, Hk=2), dict(L=-1),
+    dict(scale=0.0), dict(scale=-1.0), dict(scale=float("inf")), dict(scale=float("nan")),
+    dict(chunk=-1), dict(reserved=1), dict(B=1 << 40, T=1 << 30, Hq=1 << 20, Hk=1 << 20),
+]
+UNSUPPORTED_PROBLEMS = [
+    dict(d=32), dict(d=96), dict(d=256), dict(dtype=7), dict(L=mb.MODA_MAX_L + 1),
+    dict(Hq=6, Hk=2), dict(Hq=64, Hk=1), dict(T=(1 << 24) + 1),
+]
+
+
+@pytest.mark.parametrize("kw", INVALID_PROBLEMS)
+def test_fwd_invalid_problem(kw):
+    assert fwd_rc(prob(**kw)) == mb.MODA_ERR_INVALID_ARGUMENT
+    assert mb.load().moda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw", UNSUPPORTED_PROBLEMS)
+def test_fwd_unsupported_problem(kw):
+    assert fwd_rc(prob(**kw)) == mb.MODA_ERR_UNSUPPORTED
+
+
+def test_fwd_null_problem():
+    assert mb.load().moda_fwd(None, A, A, A, A, A, A, A, None) == mb.MODA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("which", range(7))
+@pytest.mark.parametrize("bad", [None, MIS])
+def test_fwd_bad_pointer(which, bad):
+    ptrs = [A] * 7
+    ptrs[which] = bad
+    assert fwd_rc(prob(), ptrs) == mb.MODA_ERR_INVALID_ARGUMENT
+    assert mb.load().moda_last_error().decode()
+
+
+def test_fwd_null_depth_rejected_only_when_L_positive():
+    assert fwd_rc(prob(L=3), (A, A, A, None, None, A, A)) == mb.MODA_ERR_INVALID_ARGUMENT
+    assert fwd_rc(prob(L=0, d=32), (A, A, A, None, None, A, A)) == mb.MODA_ERR_UNSUPPORTED
+
+
+def test_workspace_bytes():
+    p = prob(B=2, Hq=8, Hk=4, T=100)
+    n = mb.moda_bwd_workspace_bytes(p)
+    assert n >= 2 * 8 * 100 * 4 and n % 256 == 0
+    assert mb.moda_bwd_workspace_bytes(prob(B=0)) == 0
+    assert mb.load().moda_bwd_workspace_bytes(None) == 0
+
+
+def bwd_rc(p, ws=0x20000, ws_bytes=1 << 30, ptrs=None):
+    ptrs = ptrs or [A] * 13
+    return mb.load().moda_bwd(ctypes.byref(p), *ptrs, ws, ws_bytes, None)
+
+
+def test_bwd_workspace_checks():
+    p = prob()
+    need = mb.moda_bwd_workspace_bytes(p)
+    assert bwd_rc(p, ws=None) == mb.MODA_ERR_INVALID_ARGUMENT
+    assert bwd_rc(p, ws=0x20010) == mb.MODA_ERR_INVALID_ARGUMENT      # not 256-aligned
+    assert bwd_rc(p, ws_bytes=need - 1) == mb.MODA_ERR_INVALID_ARGUMENT
+    assert "smaller" in mb.load().moda_last_error().decode()
+
+
+@pytest.mark.parametrize("which", range(13))
+def test_bwd_bad_pointer(which):
+    ptrs = [A] * 13
+    ptrs[which] = None
+    assert bwd_rc(prob(), ptrs=ptrs) == mb.MODA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", INVALID_PROBLEMS)
+def test_bwd_invalid_problem(kw):
+    assert bwd_rc(prob(**kw)) == mb.MODA_ERR_INVALID_ARGUMENT
+
+
+def test_pack_checks():
+    lib = mb.load()
+    p = prob(L=0)
+    assert lib.moda_pack_depth(ctypes.byref(p), A, A, None) == mb.MODA_ERR_INVALID_ARGUMENT
+    p = prob(d=4)  # 8-byte bf16 rows
+    assert lib.moda_pack_depth(ctypes.byref(p), A, A, None) == mb.MODA_ERR_UNSUPPORTED
+    p = prob()
+    assert lib.moda_pack_depth(ctypes.byref(p), None, A, None) == mb.MODA_ERR_INVALID_ARGUMENT
+    assert lib.moda_pack_depth(ctypes.byref(p), A, MIS, None) == mb.MODA_ERR_INVALID_ARGUMENT
+
+
+def test_chunk_tokens_and_status_strings():
+    assert mb.moda_fwd_chunk_tokens(prob(Hq=4, Hk=2)) == 128
+    assert mb.moda_fwd_chunk_tokens(prob(Hq=4, Hk=2, chunk=64)) == 64
+    assert mb.moda_fwd_chunk_tokens(prob(Hq=16, Hk=4, chunk=64)) == 64
+    assert mb.moda_fwd_chunk_tokens(prob(Hq=16, Hk=4, chunk=16)) == 32
+    assert mb.moda_fwd_chunk_tokens(prob(dtype=mb.MODA_F32)) == 1
+    assert mb.moda_fwd_chunk_tokens(prob(d=32)) == 0
+    lib = mb.load()
+    for code, name in [(0, "MODA_OK"), (1, "MODA_ERR_INVALID_ARGUMENT"),
+                       (2, "MODA_ERR_UNSUPPORTED"), (3, "MODA_ERR_HIP")]:
+        assert lib.moda_status_string(code).decode() == name
+
+
+def test_binding_raises_moda_error():
+    with pytest.raises(mb.ModaError) as e:
+        mb._check(mb.MODA_ERR_INVALID_ARGUMENT)
+    assert e.value.status == mb.MODA_ERR_INVALID_ARGUMENT

@@ -1,0 +1,252 @@
+"""GPU parity: libmoda (through the C ABI) against the CPU oracle, element by
+element, on the same seeded inputs.
+
+Small and medium workloads are compared in full; the 64K-token workload on
+sampled query rows (forward rows are independent, so each sampled row is
+exact) and on gradients the oracle computes exactly from a subset of rows;
+invariants of the definition cover the rest at full size."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from transformer_attention_moda_amd import binding, inputs
+from parity import (check, gather_rows, host, oracle_inputs, rows_array, run_bwd, run_fwd, to64)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+W = inputs.WORKLOADS
+
+
+def fwd_full_check(w, x, chunk=0, label="", edge=False):
+    O, lse = run_fwd(x, w, chunk)
+    torch.cuda.synchronize()
+    h = oracle_inputs(x)
+    Or, lr = oracle.fwd(h["Q"], h["K"], h["V"], h.get("Kd"), h.get("Vd"), w.L, w.scale)
+    check(f"{w.name}{label} O", to64(O), Or, w.dtype, edge=edge)
+    check(f"{w.name}{label} lse", to64(lse), lr, w.dtype, edge=edge)
+    return O, lse
+
+
+def bwd_full_check(w, x, O, lse, chunk=0, label="", edge=False):
+    dQ, dK, dV, dKd, dVd = run_bwd(x, w, O, lse, chunk)
+    torch.cuda.synchronize()
+    h = oracle_inputs(x)
+    g = oracle.bwd(h["Q"], h["K"], h["V"], h.get("Kd"), h.get("Vd"), h["dO"], w.L, w.scale)
+    got = {"dQ": dQ, "dK": dK, "dV": dV}
+    if w.L > 0:
+        got.update(dKd=dKd, dVd=dVd)
+    for k, v in got.items():
+        check(f"{w.name}{label} {k}", to64(v), g[k], w.dtype, edge=edge)
+
+
+# ---------------- the five workloads ----------------
+
+def test_tiny_fp32_forward_and_backward():
+    w = W["tiny_fp32"]
+    x = inputs.make(w, seed=1, device=DEV, names=("Q", "K", "V", "Kd", "Vd", "dO"))
+    O, lse = fwd_full_check(w, x)
+    bwd_full_check(w, x, O, lse)
+
+
+def test_small_model_forward_full():
+    w = W["small_model"]
+    x = inputs.make(w, seed=2, device=DEV)
+    fwd_full_check(w, x)
+
+
+def test_layer_1p5b_forward_one_kv_group_and_no_depth_path():
+    w = W["layer_1p5b_8k"]
+    x = inputs.make(w, seed=3, device=DEV)
+    h = oracle_inputs(x)
+    G, kv = w.G, 2
+    rows = rows_array(1, w.Hq, range(w.T), heads=range(kv * G, (kv + 1) * G))
+    for L in (w.L, 0):
+        O, lse = binding.fwd(x["Q"], x["K"], x["V"], x["Kd"] if L else None,
+                             x["Vd"] if L else None, L, w.scale)
+        torch.cuda.synchronize()
+        Or, lr = oracle.fwd_rows(h["Q"], h["K"], h["V"], h["Kd"], h["Vd"], L, w.scale, rows)
+        check(f"{w.name} L={L} O (kv group {kv})", gather_rows(O, rows), Or, w.dtype)
+        check(f"{w.name} L={L} lse (kv group {kv})", gather_rows(lse, rows)[:, None],
+              lr[:, None], w.dtype)
+
+
+def long_rows(w):
+    T = w.T
+    tokens = set(range(64)) | set(range(T - 64, T)) | set(np.linspace(0, T - 1, 48).astype(int))
+    for c in (1, 7, 100, 255, 256, 511):
+        for dt in (-1, 0, 1):
+            t = c * 128 + dt
+            if 0 <= t < T:
+                tokens.add(t)
+    return sorted(tokens)
+
+
+def test_long_64k_forward_sampled_rows():
+    w = W["long_64k"]
+    x = inputs.make(w, seed=4, device=DEV)
+    O, lse = run_fwd(x, w)
+    torch.cuda.synchronize()
+    rows = rows_array(1, w.Hq, long_rows(w))
+    h = oracle_inputs(x)
+    Or, lr = oracle.fwd_rows(h["Q"], h["K"], h["V"], h["Kd"], h["Vd"], w.L, w.scale, rows)
+    check(f"{w.name} O ({len(rows)} sampled rows)", gather_rows(O, rows), Or, w.dtype)
+    check(f"{w.name} lse ({len(rows)} sampled rows)", gather_rows(lse, rows)[:, None],
+          lr[:, None], w.dtype)
+
+
+def test_train_4k_forward_backward_two_kv_groups():
+    w = W["train_4k"]
+    x = inputs.make(w, seed=5, device=DEV, names=("Q", "K", "V", "Kd", "Vd", "dO"))
+    O, lse = run_fwd(x, w)
+    dQ, dK, dV, dKd, dVd = run_bwd(x, w, O, lse)
+    torch.cuda.synchronize()
+    h = oracle_inputs(x)
+    G = w.G
+    for b, kv in ((0, 0), (3, 7)):
+        g = oracle.bwd_group(h["Q"], h["K"], h["V"], h["Kd"], h["Vd"], h["dO"], w.L, w.scale,
+                             b, kv)
+        hs = slice(kv * G, (kv + 1) * G)
+        tag = f"{w.name} (b={b}, kv={kv})"
+        check(f"{tag} O", to64(O[b, hs]), g["O"], w.dtype)
+        check(f"{tag} lse", to64(lse[b, hs]), g["lse"], w.dtype)
+        check(f"{tag} dQ", to64(dQ[b, hs]), g["dQ"], w.dtype)
+        check(f"{tag} dK", to64(dK[b, kv]), g["dK"], w.dtype)
+        check(f"{tag} dV", to64(dV[b, kv]), g["dV"], w.dtype)
+        check(f"{tag} dKd", to64(dKd[b, kv]), g["dKd"], w.dtype)
+        check(f"{tag} dVd", to64(dVd[b, kv]), g["dVd"], w.dtype)
+
+
+# ---------------- edge cases (full oracle) ----------------
+
+EDGE = [
+    # B, Hq, Hk, T, d, L
+    (1, 2, 1, 1, 64, 3),        # a single token
+    (1, 4, 2, 77, 128, 0),      # no depth, ragged T
+    (2, 8, 8, 130, 64, 1),      # G = 1
+    (1, 32, 1, 50, 128, 2),     # G = 32: one token per wave
+    (1, 16, 2, 333, 128, 7),    # G = 8, ragged
+    (1, 4, 1, 257, 64, 5),      # G = 4, one past a tile
+    (1, 2, 2, 64, 128, 1),      # exactly one tile
+    (2, 4, 2, 300, 128, 24),    # chunk boundaries inside tokens of the depth blocks
+]
+
+
+@pytest.mark.parametrize("shape", EDGE, ids=lambda s: "B{}Hq{}Hk{}T{}d{}L{}".format(*s))
+@pytest.mark.parametrize("chunk", [0, 16])
+def test_edge_shapes_forward_backward(shape, chunk):
+    B, Hq, Hk, T, d, L = shape
+    w = inputs.Workload("edge", B, Hq, Hk, T, d, L, chunk=chunk, dtype="bf16")
+    x = inputs.make(w, seed=sum(shape) + chunk, device=DEV,
+                    names=("Q", "K", "V", "Kd", "Vd", "dO"))
+    O, lse = fwd_full_check(w, x, chunk, label=f" {shape} c{chunk}", edge=True)
+    bwd_full_check(w, x, O, lse, chunk, label=f" {shape} c{chunk}", edge=True)
+
+
+@pytest.mark.parametrize("shape", [(1, 4, 2, 37, 64, 3), (2, 2, 1, 65, 128, 0),
+                                   (1, 8, 2, 20, 128, 9)])
+def test_fp32_edge_shapes(shape):
+    B, Hq, Hk, T, d, L = shape
+    w = inputs.Workload("edge_f32", B, Hq, Hk, T, d, L, chunk=0, dtype="f32")
+    x = inputs.make(w, seed=7 + T, device=DEV, names=("Q", "K", "V", "Kd", "Vd", "dO"))
+    O, lse = fwd_full_check(w, x)
+    bwd_full_check(w, x, O, lse)
+
+
+# ---------------- invariants on the GPU ----------------
+
+def test_chunk_size_does_not_change_the_result():
+    w = W["small_model"]
+    x = inputs.make(w, seed=8, device=DEV)
+    O1, l1 = run_fwd(x, w, chunk=64)     # 128 folded rows per workgroup
+    O2, l2 = run_fwd(x, w, chunk=128)    # 256 folded rows per workgroup
+    torch.cuda.synchronize()
+    assert binding.moda_fwd_chunk_tokens(binding.problem_for(x["Q"], x["K"], w.L, chunk=64)) \
+        != binding.moda_fwd_chunk_tokens(binding.problem_for(x["Q"], x["K"], w.L, chunk=128))
+    check("chunk 64 vs 128 O", to64(O1), to64(O2), "bf16")
+    check("chunk 64 vs 128 lse", to64(l1), to64(l2), "bf16")
+
+
+def test_depth_slot_permutation_invariance():
+    w = inputs.Workload("perm", 1, 8, 4, 500, 128, 6, chunk=0, dtype="bf16")
+    x = inputs.make(w, seed=9, device=DEV)
+    perm = torch.randperm(w.L, generator=torch.Generator().manual_seed(3))
+    idx = (torch.arange(w.T)[:, None] * w.L + perm[None, :]).reshape(-1).to(DEV)
+    xp = dict(x, Kd=x["Kd"][:, :, idx].contiguous(), Vd=x["Vd"][:, :, idx].contiguous())
+    O1, l1 = run_fwd(x, w)
+    O2, l2 = run_fwd(xp, w)
+    torch.cuda.synchronize()
+    check("depth-permuted O", to64(O2), to64(O1), "bf16")
+    check("depth-permuted lse", to64(l2), to64(l1), "bf16")
+
+
+def test_sequence_to_minus_infinity_gives_depth_attention():
+    # Q_t = a e1 + q', K_j = -a e1 + k', depth keys orthogonal to e1; a = 32 is exact in bf16.
+    w = inputs.Workload("seqinf", 1, 4, 2, 300, 128, 5, chunk=0, dtype="bf16")
+    x = inputs.make(w, seed=10, device=DEV)
+    x["Q"][..., 0] = 32.0
+    x["K"][..., 0] = -32.0
+    x["Kd"][..., 0] = 0.0
+    O, lse = run_fwd(x, w)
+    torch.cuda.synchronize()
+    q = to64(x["Q"])[0]
+    kd = to64(x["Kd"])[0]
+    vd = to64(x["Vd"])[0]
+    ref = np.zeros((w.Hq, w.T, w.d))
+    for h in range(w.Hq):
+        kv = h // w.G
+        u = np.einsum("tld,td->tl", kd[kv].reshape(w.T, w.L, w.d), q[h]) * w.scale
+        p = np.exp(u - u.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        ref[h] = np.einsum("tl,tld->td", p, vd[kv].reshape(w.T, w.L, w.d))
+    check("sequence at -inf: O equals depth-only attention", to64(O)[0], ref, "bf16")
+
+
+def test_forward_is_deterministic():
+    w = W["small_model"]
+    x = inputs.make(w, seed=11, device=DEV)
+    O1, l1 = run_fwd(x, w)
+    O2, l2 = run_fwd(x, w)
+    torch.cuda.synchronize()
+    assert torch.equal(O1.view(torch.int16), O2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_outputs_stay_inside_their_buffers():
+    w = inputs.Workload("canary", 1, 4, 2, 157, 128, 3, chunk=0, dtype="bf16")
+    x = inputs.make(w, seed=12, device=DEV, names=("Q", "K", "V", "Kd", "Vd", "dO"))
+    pad = 4096
+    guard = -12345.0
+
+    def guarded(shape, dtype):
+        n = int(np.prod(shape))
+        buf = torch.full((n + 2 * pad,), guard, device=DEV, dtype=dtype)
+        return buf, buf[pad:pad + n].view(shape)
+
+    ob, O = guarded(x["Q"].shape, torch.bfloat16)
+    lb, lse = guarded(x["Q"].shape[:3], torch.float32)
+    p = binding.problem_for(x["Q"], x["K"], w.L, w.scale)
+    binding.moda_fwd(p, x["Q"], x["K"], x["V"], x["Kd"], x["Vd"], O, lse)
+    grads = [guarded(x[k].shape, torch.bfloat16) for k in ("Q", "K", "V", "Kd", "Vd")]
+    ws = torch.empty(binding.moda_bwd_workspace_bytes(p), device=DEV, dtype=torch.uint8)
+    binding.moda_bwd(p, x["Q"], x["K"], x["V"], x["Kd"], x["Vd"], O, lse, x["dO"],
+                     *[g[1] for g in grads], ws)
+    torch.cuda.synchronize()
+    for buf in [ob, lb] + [g[0] for g in grads]:
+        assert torch.all(buf[:pad] == guard) and torch.all(buf[-pad:] == guard)
+
+
+# ---------------- depth packer ----------------
+
+@pytest.mark.parametrize("shape", [(3, 1, 2, 5, 128), (24, 2, 3, 77, 64), (1, 1, 1, 1, 128),
+                                   (32, 1, 8, 512, 128)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_pack_depth_is_an_exact_transpose(shape, dtype):
+    L, B, Hk, T, d = shape
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    layers = inputs.normal(shape, seed=L + T, tensor="layers_K", device=DEV, dtype=tdt)
+    packed = binding.pack_depth(layers)
+    torch.cuda.synchronize()
+    lh = host(layers)
+    expect = np.ascontiguousarray(np.transpose(lh, (1, 2, 3, 0, 4))).reshape(B, Hk, T * L, d)
+    assert np.array_equal(host(packed), expect)

@@ -1,0 +1,231 @@
+// libmoda C ABI: argument validation and dispatch (see include/moda.h).
+//
+// Every check below runs on the host before anything is enqueued, so an
+// invalid call returns its status without touching the device.
+#include "moda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moda_status_t fail(moda_status_t s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Largest sizes the kernels' 32-bit token and row indices accept.
+constexpr int64_t kMaxT = int64_t(1) << 24;
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+
+int64_t elem_size(int32_t dtype) { return dtype == MODA_BF16 ? 2 : 4; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out)
+{
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+// Common shape checks.  need_head_dim: d must be 64 or 128 (attention kernels).
+moda_status_t check_problem(const moda_problem_t* p, bool need_head_dim, moda::Shape* s)
+{
+    if (!p) return fail(MODA_ERR_INVALID_ARGUMENT, "problem pointer is NULL");
+    if (p->B < 1 || p->Hq < 1 || p->Hk < 1 || p->T < 1 || p->d < 1)
+        return fail(MODA_ERR_INVALID_ARGUMENT, "B, Hq, Hk, T and d must be >= 1 (got %lld %lld %lld %lld %lld)",
+                    (long long)p->B, (long long)p->Hq, (long long)p->Hk, (long long)p->T,
+                    (long long)p->d);
+    if (p->Hq % p->Hk != 0)
+        return fail(MODA_ERR_INVALID_ARGUMENT, "Hq (%lld) is not a multiple of Hk (%lld)",
+                    (long long)p->Hq, (long long)p->Hk);
+    if (p->L < 0) return fail(MODA_ERR_INVALID_ARGUMENT, "L must be >= 0 (got %lld)", (long long)p->L);
+    if (!std::isfinite(p->scale) || !(p->scale > 0.f))
+        return fail(MODA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
+    if (p->reserved != 0) return fail(MODA_ERR_INVALID_ARGUMENT, "reserved field must be 0");
+    if (p->chunk < 0) return fail(MODA_ERR_INVALID_ARGUMENT, "chunk must be >= 0");
+    if (p->dtype != MODA_BF16 && p->dtype != MODA_F32)
+        return fail(MODA_ERR_UNSUPPORTED, "unknown dtype %d", (int)p->dtype);
+    int64_t n = 0;
+    if (!mul_ok(p->B, p->Hq, &n) || !mul_ok(n, p->T, &n) || !mul_ok(n, p->d, &n) ||
+        !mul_ok(n, elem_size(p->dtype), &n) || !mul_ok(p->B, p->Hk, &n) || !mul_ok(n, p->T, &n) ||
+        !mul_ok(n, p->L > 0 ? p->L : 1, &n) || !mul_ok(n, p->d, &n) ||
+        !mul_ok(n, elem_size(p->dtype), &n))
+        return fail(MODA_ERR_INVALID_ARGUMENT, "tensor sizes overflow int64");
+    if (need_head_dim && p->d != 64 && p->d != 128)
+        return fail(MODA_ERR_UNSUPPORTED, "head dimension %lld not supported (64 or 128)",
+                    (long long)p->d);
+    if (p->L > MODA_MAX_L)
+        return fail(MODA_ERR_UNSUPPORTED, "L = %lld exceeds MODA_MAX_L = %d", (long long)p->L,
+                    MODA_MAX_L);
+    const int64_t G = p->Hq / p->Hk;
+    if (32 % G != 0)
+        return fail(MODA_ERR_UNSUPPORTED, "GQA group size G = %lld must divide 32", (long long)G);
+    if (p->T > kMaxT || p->T * (p->L > 0 ? p->L : 1) > kMaxRows || p->B * p->Hq > kMaxRows / 64)
+        return fail(MODA_ERR_UNSUPPORTED, "sizes beyond this build's 32-bit row indices");
+    if (s) {
+        s->B = p->B; s->Hq = p->Hq; s->Hk = p->Hk; s->T = p->T; s->d = p->d; s->L = p->L;
+        s->scale = p->scale;
+        s->G = (int)G;
+    }
+    return MODA_OK;
+}
+
+moda_status_t check_ptr(const void* ptr, const char* name)
+{
+    if (!ptr) return fail(MODA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+    if (!aligned16(ptr)) return fail(MODA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+    return MODA_OK;
+}
+
+moda_status_t check_depth(const moda_problem_t* p, const void* a, const char* na, const void* b,
+                          const char* nb)
+{
+    if (p->L == 0) {
+        if ((a && !aligned16(a)) || (b && !aligned16(b)))
+            return fail(MODA_ERR_INVALID_ARGUMENT, "%s/%s not 16-byte aligned", na, nb);
+        return MODA_OK;
+    }
+    moda_status_t st = check_ptr(a, na);
+    if (st != MODA_OK) return st;
+    return check_ptr(b, nb);
+}
+
+moda_status_t hip_status(hipError_t e, const char* what)
+{
+    if (e == hipSuccess) return MODA_OK;
+    return fail(MODA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int rows_per_workgroup(const moda_problem_t* p, int G)
+{
+    if (p->chunk == 0) return 256;
+    return (int64_t)p->chunk * G >= 256 ? 256 : 128;
+}
+
+size_t bwd_ws_bytes(const moda::Shape& s)
+{
+    const size_t rows = (size_t)(s.B * s.Hq * s.T);
+    return (rows * sizeof(float) + 255) & ~size_t(255);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moda_status_string(moda_status_t s)
+{
+    switch (s) {
+    case MODA_OK: return "MODA_OK";
+    case MODA_ERR_INVALID_ARGUMENT: return "MODA_ERR_INVALID_ARGUMENT";
+    case MODA_ERR_UNSUPPORTED: return "MODA_ERR_UNSUPPORTED";
+    case MODA_ERR_HIP: return "MODA_ERR_HIP";
+    }
+    return "unknown moda_status_t";
+}
+
+const char* moda_last_error(void) { return g_err; }
+
+int32_t moda_fwd_chunk_tokens(const moda_problem_t* p)
+{
+    moda::Shape s;
+    if (check_problem(p, true, &s) != MODA_OK) return 0;
+    if (p->dtype == MODA_F32) return 1;
+    return rows_per_workgroup(p, s.G) / s.G;
+}
+
+moda_status_t moda_fwd(const moda_problem_t* p, const void* Q, const void* K, const void* V,
+                       const void* Kd, const void* Vd, void* O, float* lse, void* stream)
+{
+    moda::Shape s;
+    moda_status_t st = check_problem(p, true, &s);
+    if (st != MODA_OK) return st;
+    const void* ptrs[] = {Q, K, V, O, lse};
+    const char* names[] = {"Q", "K", "V", "O", "lse"};
+    for (int i = 0; i < 5; ++i)
+        if ((st = check_ptr(ptrs[i], names[i])) != MODA_OK) return st;
+    if ((st = check_depth(p, Kd, "Kd", Vd, "Vd")) != MODA_OK) return st;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (p->dtype == MODA_BF16)
+        e = moda::launch_fwd_bf16(s, Q, K, V, Kd, Vd, O, lse, rows_per_workgroup(p, s.G), hs);
+    else
+        e = moda::launch_fwd_f32(s, (const float*)Q, (const float*)K, (const float*)V,
+                                 (const float*)Kd, (const float*)Vd, (float*)O, lse, hs);
+    return hip_status(e, "moda_fwd launch");
+}
+
+size_t moda_bwd_workspace_bytes(const moda_problem_t* p)
+{
+    moda::Shape s;
+    if (check_problem(p, true, &s) != MODA_OK) return 0;
+    return bwd_ws_bytes(s);
+}
+
+moda_status_t moda_bwd(const moda_problem_t* p, const void* Q, const void* K, const void* V,
+                       const void* Kd, const void* Vd, const void* O, const float* lse,
+                       const void* dO, void* dQ, void* dK, void* dV, void* dKd, void* dVd,
+                       void* workspace, size_t workspace_bytes, void* stream)
+{
+    moda::Shape s;
+    moda_status_t st = check_problem(p, true, &s);
+    if (st != MODA_OK) return st;
+    const void* ptrs[] = {Q, K, V, O, lse, dO, dQ, dK, dV};
+    const char* names[] = {"Q", "K", "V", "O", "lse", "dO", "dQ", "dK", "dV"};
+    for (int i = 0; i < 9; ++i)
+        if ((st = check_ptr(ptrs[i], names[i])) != MODA_OK) return st;
+    if ((st = check_depth(p, Kd, "Kd", Vd, "Vd")) != MODA_OK) return st;
+    if ((st = check_depth(p, dKd, "dKd", dVd, "dVd")) != MODA_OK) return st;
+    if (!workspace) return fail(MODA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(MODA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    const size_t need = bwd_ws_bytes(s);
+    if (workspace_bytes < need)
+        return fail(MODA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu required",
+                    workspace_bytes, need);
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (p->dtype == MODA_BF16)
+        e = moda::launch_bwd_bf16(s, Q, K, V, Kd, Vd, O, lse, dO, dQ, dK, dV, dKd, dVd,
+                                  (float*)workspace, hs);
+    else
+        e = moda::launch_bwd_f32(s, (const float*)Q, (const float*)K, (const float*)V,
+                                 (const float*)Kd, (const float*)Vd, (const float*)O, lse,
+                                 (const float*)dO, (float*)dQ, (float*)dK, (float*)dV,
+                                 (float*)dKd, (float*)dVd, (float*)workspace, hs);
+    return hip_status(e, "moda_bwd launch");
+}
+
+moda_status_t moda_pack_depth(const moda_problem_t* p, const void* layers, void* packed,
+                              void* stream)
+{
+    moda::Shape s;
+    moda_status_t st = check_problem(p, false, &s);
+    if (st != MODA_OK) return st;
+    if (p->L < 1) return fail(MODA_ERR_INVALID_ARGUMENT, "moda_pack_depth needs L >= 1");
+    const int64_t row_bytes = p->d * elem_size(p->dtype);
+    if (row_bytes % 16 != 0)
+        return fail(MODA_ERR_UNSUPPORTED, "row of %lld bytes is not a multiple of 16",
+                    (long long)row_bytes);
+    if ((st = check_ptr(layers, "layers")) != MODA_OK) return st;
+    if ((st = check_ptr(packed, "packed")) != MODA_OK) return st;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    return hip_status(moda::launch_pack_depth(p->L, p->B, p->Hk, p->T, row_bytes, layers, packed, hs),
+                      "moda_pack_depth launch");
+}
+
+}  // extern "C"

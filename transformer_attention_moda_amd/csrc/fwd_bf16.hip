@@ -1,0 +1,342 @@
+// MoDA forward, bfloat16 storage, for gfx950.
+//
+// One workgroup owns one query chunk of one KV group: BM = 32*NW folded query
+// rows i_q = t*G + g of batch b and KV head kv (the folded index and the
+// grouped causal mask floor(i_q/G) >= i_k of "Mixture-of-Depths Attention",
+// arXiv 2603.15619, paper summary, section 3.4 "The Unified Operator").  Each
+// of the NW waves owns 32 consecutive folded rows, i.e. 32/G whole tokens with
+// all G heads, as the 32 columns of its MFMA tiles.
+//
+// Sequence phase: K and V tiles of BN = 64 keys are staged in LDS (row-major,
+// coalesced 16-byte loads, double-buffered) and shared by the NW waves and so
+// by the G heads.  Per tile a wave computes S^T = K Q^T with 32x32x16 bf16 MFMA
+// (fp32 accumulate), updates the online-softmax state (running max m, running
+// sum, output accumulator o) with exp2, and accumulates O^T += V^T P^T with the
+// V operand read transposed out of LDS (ds_read_b64_tr_b16).  Tiles entirely
+// before the wave's first token skip the mask; later ones apply j <= t
+// (the two sequence loops of the paper summary's "Hardware-Efficient
+// Implementation", "Fused online-softmax (Algorithm 1)").
+//
+// Depth phase: each wave then reads only the depth rows of its own tokens,
+// rows [t_lo*L, (t_hi+1)*L) of the token-major flattened depth KV, in blocks
+// of 32 rows, masks with floor(r/L) == t (depth matching mask), and folds them
+// into the same online-softmax state (group-aware depth loop of the same
+// section).  The wave's columns hold all G heads of each token, so every depth
+// row is fetched from HBM once and serves its G query rows through the MFMA.
+//
+// Epilogue: O = o / sum in bf16 (round to nearest even) and
+// lse = scale*m + ln(sum) in fp32.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moda {
+namespace {
+
+struct FwdArgs {
+    const uint16_t* Q;
+    const uint16_t* K;
+    const uint16_t* V;
+    const uint16_t* Kd;
+    const uint16_t* Vd;
+    uint16_t* O;
+    float* lse;
+    int Hq, Hk, T, L, G;
+    int nchunks;   // query chunks per (b, kv)
+    float c;       // scale * log2(e)
+    float scale;
+};
+
+constexpr int BN = 64;  // keys per sequence tile
+
+template <int D>
+struct Tile {
+    static constexpr int KP = D + 8;  // LDS row pitch (elements): rows start 16 bytes apart in bank space
+    static constexpr int ELEMS = BN * KP;
+};
+
+// Online-softmax update of one lane's column with the scores held in s[0..NB-1]
+// (raw q.k values, 16 per block; masked entries are -inf).  On return s holds
+// the weights exp2(c*(score - m_new)) and o/l are rescaled.
+template <int D, int NB>
+__device__ __forceinline__ void softmax_update(f32x16 (&s)[2], float& m, float& l,
+                                               f32x16 (&o)[D / 32], float c)
+{
+    float mt = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mt = fmaxf(mt, s[kb][j]);
+    mt = max_halves(mt);
+    const float m_new = fmaxf(m, mt);
+    const float alpha = fast_exp2((m - m_new) * c);
+    const float mc = m_new * c;
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float p = fast_exp2(fmaf(s[kb][j], c, -mc));
+            s[kb][j] = p;
+            ps += p;
+        }
+    ps = sum_halves(ps);
+    l = l * alpha + ps;
+    m = m_new;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+}
+
+// O^T += V^T P^T for a block of 32 keys held in LDS rows [row0, row0+32) of a
+// row-major tile with pitch KP.  p holds the weights of those 32 keys
+// (S^T output layout); the V operand is read transposed so that k-slot e of
+// lane half h is key 16*sp + 8*(e/4) + 4*h + e%4, matching the P layout.
+template <int D, int KP>
+__device__ __forceinline__ void pv_block(const uint16_t* vt, int row0, const f32x16& p,
+                                         f32x16 (&o)[D / 32], int lane)
+{
+    const int col = lane & 31, hf = lane >> 5;
+    const int krow = row0 + 4 * hf + ((col & 15) >> 2);   // + 16*sp + 8*q
+    const int dcol = 16 * (col >> 4) + 4 * (col & 3);      // + 32*db
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+        const bf16x8 pb = to_bf16x8(p[8 * sp + 0], p[8 * sp + 1], p[8 * sp + 2], p[8 * sp + 3],
+                                    p[8 * sp + 4], p[8 * sp + 5], p[8 * sp + 6], p[8 * sp + 7]);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const uint16_t* base = vt + (krow + 16 * sp) * KP + dcol + 32 * db;
+            const bf16x4 lo = lds_read_tr(base);
+            const bf16x4 hi = lds_read_tr(base + 8 * KP);
+            const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            o[db] = mfma32(a, pb, o[db]);
+        }
+    }
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(FwdArgs a)
+{
+    using TL = Tile<D>;
+    constexpr int KP = TL::KP;
+    constexpr int NT = NW * 64;
+    constexpr int CH = D / 8;                  // 16-byte chunks per row
+    constexpr int LOADS = BN * CH / NT;        // per thread, per tensor, per tile
+    static_assert(BN * CH % NT == 0, "tile staging must divide evenly");
+    constexpr int BM = NW * 32;
+    // [buf][K or V][BN rows * KP]; the depth phase reuses it as NW private 32-row slices.
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TL::ELEMS];
+    static_assert(NW * 32 * KP <= 2 * 2 * TL::ELEMS, "depth slices must fit");
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int col = lane & 31, hf = lane >> 5;
+    const int G = a.G, T = a.T, L = a.L;
+
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int unit = logical / a.nchunks;
+    const int chunk = a.nchunks - 1 - logical % a.nchunks;   // heaviest chunks first
+    const int b = unit / a.Hk, kv = unit % a.Hk;
+    const int64_t TG = (int64_t)T * G;
+    const int64_t r0 = (int64_t)chunk * BM;
+    const int t_hi_wg = (int)min((r0 + BM - 1) / G, (int64_t)T - 1);
+
+    const int64_t fw = r0 + 32 * w;              // first folded row of this wave
+    const int64_t fcol = fw + col;               // this lane's column
+    const bool valid = fcol < TG;
+    const int tcol = (int)min(fcol / G, (int64_t)T - 1);
+    const int hq = kv * G + (int)(fcol % G);
+    const int tw_lo = (int)min(fw / G, (int64_t)T - 1);
+    const int tw_hi = (int)min((fw + 31) / G, (int64_t)T - 1);
+
+    const int64_t kvbase = ((int64_t)b * a.Hk + kv) * T;
+    const uint16_t* Kb = a.K + kvbase * D;
+    const uint16_t* Vb = a.V + kvbase * D;
+
+    // Q^T columns as MFMA B operands: k-step si covers d = 16*si + 8*hf .. +8.
+    bf16x8 qreg[D / 16];
+    {
+        const uint16_t* qrow = a.Q + (((int64_t)b * a.Hq + hq) * T + tcol) * D + 8 * hf;
+#pragma unroll
+        for (int si = 0; si < D / 16; ++si) {
+            uint4 v = valid ? ld16(qrow + 16 * si) : make_uint4(0, 0, 0, 0);
+            qreg[si] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
+    float m = -INFINITY, l = 0.f;
+
+    // ---- sequence phase ----
+    const int ntiles = t_hi_wg / BN + 1;
+    uint4 kst[LOADS], vst[LOADS];
+    auto gload = [&](int tile) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int c = tid + i * NT, row = c / CH, ch = c % CH;
+            const int key = tile * BN + row;
+            if (key < T) {
+                kst[i] = ld16(Kb + (int64_t)key * D + ch * 8);
+                vst[i] = ld16(Vb + (int64_t)key * D + ch * 8);
+            } else {
+                kst[i] = make_uint4(0, 0, 0, 0);
+                vst[i] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+        uint16_t* ks = smem + (2 * buf) * TL::ELEMS;
+        uint16_t* vs = ks + TL::ELEMS;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int c = tid + i * NT, row = c / CH, ch = c % CH;
+            st16(ks + row * KP + ch * 8, kst[i]);
+            st16(vs + row * KP + ch * 8, vst[i]);
+        }
+    };
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+        const int buf = it & 1;
+        if (it + 1 < ntiles) gload(it + 1);
+        const int k0 = it * BN;
+        if (k0 <= tw_hi) {
+            const uint16_t* ks = smem + (2 * buf) * TL::ELEMS;
+            const uint16_t* vs = ks + TL::ELEMS;
+            f32x16 s[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
+                const uint16_t* krow = ks + (kb * 32 + col) * KP + 8 * hf;
+#pragma unroll
+                for (int si = 0; si < D / 16; ++si) {
+                    const bf16x8 av = *(const bf16x8*)(krow + 16 * si);
+                    s[kb] = mfma32(av, qreg[si], s[kb]);
+                }
+            }
+            if (k0 + BN - 1 > tw_lo) {   // tile reaches past the wave's first token: causal mask
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int key = k0 + kb * 32 + (j >> 2) * 8 + hf * 4 + (j & 3);
+                        if (key > tcol) s[kb][j] = -INFINITY;
+                    }
+            }
+            softmax_update<D, 2>(s, m, l, o, a.c);
+            pv_block<D, KP>(vs, 0, s[0], o, lane);
+            pv_block<D, KP>(vs, 32, s[1], o, lane);
+        }
+        if (it + 1 < ntiles) sstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- depth phase: this wave's tokens only ----
+    if (L > 0) {
+        uint16_t* vslice = smem + w * 32 * KP;   // private 32-row slice of the (now idle) tiles
+        const int64_t TL_rows = (int64_t)T * L;
+        const uint16_t* Kdb = a.Kd + kvbase * (int64_t)L * D;
+        const uint16_t* Vdb = a.Vd + kvbase * (int64_t)L * D;
+        const int64_t dlo = (int64_t)tw_lo * L, dhi = (int64_t)(tw_hi + 1) * L;
+        for (int64_t rb = dlo; rb < dhi; rb += 32) {
+            // V rows of the block into the wave's slice (row-major); rows past the end are clamped.
+#pragma unroll
+            for (int i = 0; i < D / 16; ++i) {
+                const int c = lane + 64 * i, row = c / CH, ch = c % CH;
+                const int64_t r = min(rb + row, TL_rows - 1);
+                st16(vslice + row * KP + ch * 8, ld16(Vdb + r * D + ch * 8));
+            }
+            // K rows as A operands straight from HBM.
+            f32x16 s[2];
+            {
+                const int64_t r = min(rb + col, TL_rows - 1);
+                const uint16_t* krow = Kdb + r * D + 8 * hf;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) s[0][j] = 0.f;
+#pragma unroll
+                for (int si = 0; si < D / 16; ++si)
+                    s[0] = mfma32(__builtin_bit_cast(bf16x8, ld16(krow + 16 * si)), qreg[si], s[0]);
+            }
+            // Row rb + (j/4)*8 + 4*hf + j%4 is visible iff it lies in [tcol*L, tcol*L + L).
+            const int64_t lo = (int64_t)tcol * L - rb - 4 * hf;   // first visible row index
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int rj = (j >> 2) * 8 + (j & 3);
+                if (rj < lo || rj >= lo + L) s[0][j] = -INFINITY;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            softmax_update<D, 1>(s, m, l, o, a.c);
+            pv_block<D, KP>(vslice, 0, s[0], o, lane);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+    }
+
+    // ---- epilogue ----
+    if (valid) {
+        const float inv = 1.f / l;
+        uint16_t* orow = a.O + (((int64_t)b * a.Hq + hq) * T + tcol) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                bf16x4 v;
+                v[0] = (__bf16)(o[db][4 * jj + 0] * inv);
+                v[1] = (__bf16)(o[db][4 * jj + 1] * inv);
+                v[2] = (__bf16)(o[db][4 * jj + 2] * inv);
+                v[3] = (__bf16)(o[db][4 * jj + 3] * inv);
+                *(bf16x4*)(orow + 32 * db + 8 * jj + 4 * hf) = v;
+            }
+        if (hf == 0) a.lse[((int64_t)b * a.Hq + hq) * T + tcol] = a.scale * m + __logf(l);
+    }
+}
+
+template <int D, int NW>
+hipError_t launch(const Shape& s, const FwdArgs& a, int nunits, hipStream_t st)
+{
+    const int64_t grid = (int64_t)nunits * a.nchunks;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const Shape& s, const void* Q, const void* K, const void* V,
+                           const void* Kd, const void* Vd, void* O, float* lse, int rows_per_wg,
+                           hipStream_t st)
+{
+    FwdArgs a;
+    a.Q = (const uint16_t*)Q;
+    a.K = (const uint16_t*)K;
+    a.V = (const uint16_t*)V;
+    a.Kd = (const uint16_t*)Kd;
+    a.Vd = (const uint16_t*)Vd;
+    a.O = (uint16_t*)O;
+    a.lse = lse;
+    a.Hq = (int)s.Hq;
+    a.Hk = (int)s.Hk;
+    a.T = (int)s.T;
+    a.L = (int)s.L;
+    a.G = s.G;
+    a.scale = s.scale;
+    a.c = s.scale * kLog2e;
+    const int64_t TG = s.T * s.G;
+    a.nchunks = (int)((TG + rows_per_wg - 1) / rows_per_wg);
+    const int nunits = (int)(s.B * s.Hk);
+    if (s.d == 128) {
+        return rows_per_wg == 256 ? launch<128, 8>(s, a, nunits, st)
+                                  : launch<128, 4>(s, a, nunits, st);
+    }
+    return rows_per_wg == 256 ? launch<64, 8>(s, a, nunits, st) : launch<64, 4>(s, a, nunits, st);
+}
+
+}  // namespace moda
