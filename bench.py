@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""MoDA operator benchmark on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: pack the layer-major depth K and V into the
+token-major layout, run the forward (O and log-sum-exp), then the backward
+(dQ, dK, dV, dK_depth, dV_depth).  The default workload is the 64K-token long
+sequence (B=1, Hq=16, Hk=8, T=65536, d=128, L=24, bf16).
+
+Printed: one JSON line.  `value` is algorithmic forward+backward TFLOP/s of
+the whole step (forward FLOP = 4 d B Hq (T(T+1)/2 + T L), backward = 2.5x
+forward); the same step with L=0 (no depth: plain causal attention through
+the same entry points) gives the overhead of the depth path.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (published)
+HBM_PEAK_GBS = 8000.0             # MI355X HBM3E (published)
+
+
+def fwd_flops(w, L=None):
+    L = w.L if L is None else L
+    pairs = w.T * (w.T + 1) // 2 + w.T * L
+    return 4.0 * w.d * w.B * w.Hq * pairs
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_64k")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-l0", action="store_true", help="skip the L=0 comparison run")
+    return ap.parse_args()
+
+
+class Step:
+    """Buffers and the launches of one step, with per-entry-point events."""
+
+    def __init__(self, w, L, seed=0):
+        import torch
+        from transformer_attention_moda_amd import binding, inputs
+        self.torch, self.mb, self.w, self.L = torch, binding, w, L
+        dev = "cuda:0"
+        names = ["Q", "K", "V", "dO"] + (["layers_K", "layers_V"] if L > 0 else [])
+        x = inputs.make(w.with_(L=L), seed=seed, device=dev, names=names)
+        self.x = x
+        self.p = binding.problem_for(x["Q"], x["K"], L, w.scale, chunk=0)
+        B, Hk, T, d = w.B, w.Hk, w.T, w.d
+        empty = lambda shape: torch.empty(shape, device=dev, dtype=torch.bfloat16)  # noqa: E731
+        self.Kd = empty((B, Hk, T * L, d)) if L > 0 else None
+        self.Vd = empty((B, Hk, T * L, d)) if L > 0 else None
+        self.O = torch.empty_like(x["Q"])
+        self.lse = torch.empty((w.B, w.Hq, T), device=dev, dtype=torch.float32)
+        self.dQ, self.dK, self.dV = (torch.empty_like(x["Q"]), torch.empty_like(x["K"]),
+                                     torch.empty_like(x["V"]))
+        self.dKd = torch.empty_like(self.Kd) if L > 0 else None
+        self.dVd = torch.empty_like(self.Vd) if L > 0 else None
+        nws = binding.moda_bwd_workspace_bytes(self.p)
+        self.ws = torch.empty(max(nws, 256), device=dev, dtype=torch.uint8)
+        if L > 0:
+            self.pp = binding.problem(B, Hk, Hk, T, d, L, 1.0, binding.MODA_BF16)
+        self.events = []
+
+    def run(self, record=False):
+        torch, mb, x = self.torch, self.mb, self.x
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        if record:
+            ev[0].record()
+        if self.L > 0:
+            mb.moda_pack_depth(self.pp, x["layers_K"], self.Kd)
+            mb.moda_pack_depth(self.pp, x["layers_V"], self.Vd)
+        if record:
+            ev[1].record()
+        mb.moda_fwd(self.p, x["Q"], x["K"], x["V"], self.Kd, self.Vd, self.O, self.lse)
+        if record:
+            ev[2].record()
+        mb.moda_bwd(self.p, x["Q"], x["K"], x["V"], self.Kd, self.Vd, self.O, self.lse, x["dO"],
+                    self.dQ, self.dK, self.dV, self.dKd, self.dVd, self.ws)
+        if record:
+            ev[3].record()
+            self.events.append(ev)
+
+    def timed(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.run()
+        torch.cuda.synchronize()
+        self.events = []
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        t0.record()
+        for _ in range(steps):
+            self.run(record=True)
+        t1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        total_ms = t0.elapsed_time(t1)
+        parts = {"pack": 0.0, "fwd": 0.0, "bwd": 0.0}
+        for ev in self.events:
+            parts["pack"] += ev[0].elapsed_time(ev[1])
+            parts["fwd"] += ev[1].elapsed_time(ev[2])
+            parts["bwd"] += ev[2].elapsed_time(ev[3])
+        return total_ms / steps, {k: v / steps for k, v in parts.items()}, wall
+
+
+def cpu_baseline(w, step, seconds):
+    """Time the CPU oracle on a bounded sample of the same workload: the full
+    forward+backward of the last n tokens of one KV group (G query heads)."""
+    import numpy as np
+    import oracle
+    from transformer_attention_moda_amd import inputs as inp
+    x = step.x
+    G, T, L, d = w.G, w.T, w.L, w.d
+    th = oracle.num_threads()
+
+    def sample(n):
+        t_lo = T - n
+        sub = {
+            "Q": inp.to_host_storage(x["Q"][:1, :G]),
+            "dO": inp.to_host_storage(x["dO"][:1, :G]),
+            "K": inp.to_host_storage(x["K"][:1, :1]),
+            "V": inp.to_host_storage(x["V"][:1, :1]),
+        }
+        for name, src in (("Kd", step.Kd), ("Vd", step.Vd)):
+            full = np.zeros((1, 1, T * L, d), np.uint16)
+            full[0, 0, t_lo * L:] = inp.to_host_storage(src[0, 0, t_lo * L:])
+            sub[name] = full
+        t0 = time.perf_counter()
+        oracle.bwd_group(sub["Q"], sub["K"], sub["V"], sub["Kd"], sub["Vd"], sub["dO"], L,
+                         w.scale, 0, 0, t_lo, T)
+        dt = time.perf_counter() - t0
+        pairs = sum(t + 1 + L for t in range(t_lo, T)) * G
+        return dt, 3.5 * 4.0 * d * pairs, t_lo
+
+    sample(1)                      # start the OpenMP pool
+    dt, fl, _ = sample(8)
+    n = int(max(8, min(T, 8 * seconds / max(dt, 1e-3))))
+    dt, fl, t_lo = sample(n)
+    return {
+        "value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": th, "kind": "oracle",
+        "sample": (f"fp64 forward+backward of tokens {t_lo}..{T - 1} of one KV group "
+                   f"({G} query heads, b=0, kv=0) of the {w.name} workload; "
+                   f"{dt:.1f} s on {th} threads; algorithmic FLOP of the sample "
+                   f"(3.5 x 4 d x visible pairs) / wall time"),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    from transformer_attention_moda_amd import binding, inputs
+    binding.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = inputs.WORKLOADS[args.workload]
+
+    step = Step(w, w.L, seed=0)
+    ms, parts, wall = step.timed(args.steps, args.warmup)
+    f_fwd, f_all = fwd_flops(w), 3.5 * fwd_flops(w)
+    value = f_all / (ms * 1e-3) / 1e12
+
+    res0 = None
+    if not args.no_l0:
+        del step.x["layers_K"], step.x["layers_V"]
+        torch.cuda.empty_cache()
+        s0 = Step(w, 0, seed=0)
+        ms0, parts0, _ = s0.timed(args.steps, args.warmup)
+        res0 = {"ms_per_step": ms0, "fwd_ms": parts0["fwd"], "bwd_ms": parts0["bwd"]}
+        del s0
+        torch.cuda.empty_cache()
+
+    # Dominant kernel of the step and its roofline.
+    depth_bytes = 2 * w.B * w.Hk * w.T * w.L * w.d * 2
+    cand = {
+        "fwd": ("mfma", f_fwd / (parts["fwd"] * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"),
+        "bwd": ("mfma", 2.5 * f_fwd / (parts["bwd"] * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS,
+                "TFLOP/s"),
+        "pack": ("hbm", 2 * depth_bytes / (parts["pack"] * 1e-3) / 1e9 if parts["pack"] else 0,
+                 HBM_PEAK_GBS, "GB/s"),
+    }
+    dom = max(parts, key=parts.get)
+    bound, ach, peak, unit = cand[dom]
+    roof = {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+            "frac": round(ach / peak, 4), "traffic": None, "kernel": f"moda_{dom}",
+            "per_entry_point": {k: {"ms": round(parts[k], 3), "achieved": round(cand[k][1], 2),
+                                    "unit": cand[k][3], "frac": round(cand[k][1] / cand[k][2], 4)}
+                                for k in parts}}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        if step.Kd is None:
+            step = Step(w, w.L, seed=0)
+            step.run()
+            torch.cuda.synchronize()
+        cpu = cpu_baseline(w, step, args.cpu_seconds)
+
+    out = {
+        "metric": "MoDA fwd+bwd TFLOP/s bf16 at T=64K (% MFMA peak); overhead vs own L=0 path",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), bf16)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hk": w.Hk, "T": w.T, "d": w.d,
+                   "L": w.L, "step": "pack depth K,V + forward + backward",
+                   "chunk_tokens": binding.moda_fwd_chunk_tokens(step.p)},
+        "pct_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "fwd_tflops": round(f_fwd / (parts["fwd"] * 1e-3) / 1e12, 2),
+        "ms": {k: round(v, 3) for k, v in parts.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    if res0:
+        out["l0"] = {k: round(v, 3) for k, v in res0.items()}
+        out["overhead"] = {
+            "fwd": round((parts["fwd"] - res0["fwd_ms"]) / res0["fwd_ms"], 4),
+            "fwd_bwd": round((parts["fwd"] + parts["bwd"] - res0["fwd_ms"] - res0["bwd_ms"]) /
+                             (res0["fwd_ms"] + res0["bwd_ms"]), 4),
+            "step": round((ms - res0["ms_per_step"]) / res0["ms_per_step"], 4),
+            "fwd_pages_convention": round((parts["fwd"] - res0["fwd_ms"]) / parts["fwd"], 4),
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -117,10 +117,11 @@ int rows_per_workgroup(const moda_problem_t* p, int G)
     return (int64_t)p->chunk * G >= 256 ? 256 : 128;
 }
 
+// Two fp32 values per query row: the log-sum-exp in log2 units and D = <dO, O>.
 size_t bwd_ws_bytes(const moda::Shape& s)
 {
     const size_t rows = (size_t)(s.B * s.Hq * s.T);
-    return (rows * sizeof(float) + 255) & ~size_t(255);
+    return (2 * rows * sizeof(float) + 255) & ~size_t(255);
 }
 
 }  // namespace

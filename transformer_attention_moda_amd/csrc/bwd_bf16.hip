@@ -1,15 +1,579 @@
-// MoDA backward, bfloat16 storage.
+// MoDA backward, bfloat16 storage, for gfx950.
+//
+// The gradients of the operator of "Mixture-of-Depths Attention" (arXiv
+// 2603.15619, paper summary, section 3.4: one softmax over the causal
+// sequence keys and the token's own L depth keys).  With p the softmax weights
+// (recomputed from the forward's log-sum-exp), D = <dO, O> and
+// dS = p (dO.v - D) for every visible key/value pair (v in V or V_depth):
+//   dQ  = scale (sum over sequence keys of dS K + sum over own depth rows of dS Kd)
+//   dK  = scale sum over queries of dS Q,      dV  = sum over queries of p dO
+//   dKd = scale sum over the token's G heads of dS Q, dVd = same with p dO
+//
+// Four kernels, none with atomics (results are deterministic):
+//   bwd_pre    D and lse in log2 units, one per query row (workspace);
+//   bwd_dq     query-stationary like the forward: per key tile S^T = K Q^T,
+//              dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T with K read
+//              transposed from LDS; then the wave's own depth rows the same
+//              way (depth matching mask);
+//   bwd_dkdv   key-stationary: each wave keeps 32 keys of K and V as MFMA
+//              operands and walks the query rows that see them:
+//              S = Q K^T, dP = dO V^T (lane = key), dV^T += dO^T P and
+//              dK^T += Q^T dS with dO and Q read transposed from LDS;
+//   bwd_depth  per wave, its tokens' depth rows: S_d = Q Kd^T (lane = depth
+//              row), dVd^T += dO^T P_d, dKd^T += Q^T dS_d.  A token's G heads sit
+//              in one wave, so every depth row is finished by one wave.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moda {
+namespace {
+
+struct BwdArgs {
+    const uint16_t* Q;
+    const uint16_t* K;
+    const uint16_t* V;
+    const uint16_t* Kd;
+    const uint16_t* Vd;
+    const uint16_t* O;
+    const float* lse;
+    const uint16_t* dO;
+    uint16_t* dQ;
+    uint16_t* dK;
+    uint16_t* dV;
+    uint16_t* dKd;
+    uint16_t* dVd;
+    float* lse2;   // lse * log2(e), [B*Hq*T]
+    float* Dv;     // <dO, O>,        [B*Hq*T]
+    int Hq, Hk, T, L, G, lgG;
+    int nblocks;   // work blocks per (b, kv) of the launched kernel
+    float c;       // scale * log2(e)
+    float scale;
+    int64_t rows;  // B*Hq*T
+};
+
+constexpr int BN = 64;  // sequence keys per tile (bwd_dq)
+
+// ---------------------------------------------------------------- bwd_pre
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a)
+{
+    constexpr int LPR = D / 8;            // lanes per row (16 bytes each)
+    constexpr int RPB = 256 / LPR;        // rows per block
+    const int sub = threadIdx.x % LPR;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+    const bool ok = row < a.rows;
+    float acc = 0.f;
+    if (ok) {
+        const uint4 x = ld16(a.dO + row * D + sub * 8);
+        const uint4 y = ld16(a.O + row * D + sub * 8);
+        const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc += __uint_as_float(xs[i] << 16) * __uint_as_float(ys[i] << 16);
+            acc += __uint_as_float(xs[i] & 0xffff0000u) * __uint_as_float(ys[i] & 0xffff0000u);
+        }
+    }
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (ok && sub == 0) {
+        a.Dv[row] = acc;
+        a.lse2[row] = a.lse[row] * kLog2e;
+    }
+}
+
+// ---------------------------------------------------------------- bwd_dq
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
+{
+    constexpr int KP = D + 8;
+    constexpr int ELEMS = BN * KP;
+    constexpr int NT = NW * 64;
+    constexpr int CH = D / 8;
+    constexpr int LOADS = BN * CH / NT;
+    static_assert(BN * CH % NT == 0, "tile staging must divide evenly");
+    constexpr int BM = NW * 32;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * ELEMS];
+    static_assert(NW * 32 * KP <= 2 * 2 * ELEMS, "depth slices must fit");
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int col = lane & 31, hf = lane >> 5;
+    const int G = a.G, T = a.T, L = a.L;
+
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int unit = logical / a.nblocks;
+    const int chunk = a.nblocks - 1 - logical % a.nblocks;
+    const int b = unit / a.Hk, kv = unit % a.Hk;
+    const int64_t TG = (int64_t)T * G;
+    const int64_t r0 = (int64_t)chunk * BM;
+    const int t_hi_wg = (int)min((r0 + BM - 1) / G, (int64_t)T - 1);
+    const int64_t fw = r0 + 32 * w, fcol = fw + col;
+    const bool valid = fcol < TG;
+    const int tcol = (int)min(fcol / G, (int64_t)T - 1);
+    const int hq = kv * G + (int)(fcol % G);
+    const int tw_lo = (int)min(fw / G, (int64_t)T - 1);
+    const int tw_hi = (int)min((fw + 31) / G, (int64_t)T - 1);
+
+    const int64_t kvbase = ((int64_t)b * a.Hk + kv) * T;
+    const uint16_t* Kb = a.K + kvbase * D;
+    const uint16_t* Vb = a.V + kvbase * D;
+    const int64_t qrow_idx = ((int64_t)b * a.Hq + hq) * T + tcol;
+
+    bf16x8 qreg[D / 16], dreg[D / 16];
+    {
+        const uint16_t* qrow = a.Q + qrow_idx * D + 8 * hf;
+        const uint16_t* drow = a.dO + qrow_idx * D + 8 * hf;
+#pragma unroll
+        for (int si = 0; si < D / 16; ++si) {
+            qreg[si] = __builtin_bit_cast(bf16x8, valid ? ld16(qrow + 16 * si) : make_uint4(0, 0, 0, 0));
+            dreg[si] = __builtin_bit_cast(bf16x8, valid ? ld16(drow + 16 * si) : make_uint4(0, 0, 0, 0));
+        }
+    }
+    const float lse2 = valid ? a.lse2[qrow_idx] : INFINITY;
+    const float Dr = valid ? a.Dv[qrow_idx] : 0.f;
+    const float c = a.c;
+
+    f32x16 dq[D / 32];
+    zero(dq);
+
+    const int ntiles = t_hi_wg / BN + 1;
+    uint4 kst[LOADS], vst[LOADS];
+    auto gload = [&](int tile) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int cc = tid + i * NT, row = cc / CH, ch = cc % CH;
+            const int key = tile * BN + row;
+            if (key < T) {
+                kst[i] = ld16(Kb + (int64_t)key * D + ch * 8);
+                vst[i] = ld16(Vb + (int64_t)key * D + ch * 8);
+            } else {
+                kst[i] = make_uint4(0, 0, 0, 0);
+                vst[i] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+        uint16_t* ks = smem + (2 * buf) * ELEMS;
+        uint16_t* vs = ks + ELEMS;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int cc = tid + i * NT, row = cc / CH, ch = cc % CH;
+            st16(ks + row * KP + ch * 8, kst[i]);
+            st16(vs + row * KP + ch * 8, vst[i]);
+        }
+    };
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+        const int buf = it & 1;
+        if (it + 1 < ntiles) gload(it + 1);
+        const int k0 = it * BN;
+        if (k0 <= tw_hi) {
+            const uint16_t* ks = smem + (2 * buf) * ELEMS;
+            const uint16_t* vs = ks + ELEMS;
+            f32x16 s[2], dp[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) s[kb][j] = dp[kb][j] = 0.f;
+                const uint16_t* krow = ks + (kb * 32 + col) * KP + 8 * hf;
+                const uint16_t* vrow = vs + (kb * 32 + col) * KP + 8 * hf;
+#pragma unroll
+                for (int si = 0; si < D / 16; ++si) {
+                    s[kb] = mfma32(*(const bf16x8*)(krow + 16 * si), qreg[si], s[kb]);
+                    dp[kb] = mfma32(*(const bf16x8*)(vrow + 16 * si), dreg[si], dp[kb]);
+                }
+            }
+            const bool need_mask = k0 + BN - 1 > tw_lo;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int key = k0 + kb * 32 + (j >> 2) * 8 + hf * 4 + (j & 3);
+                    float p = fast_exp2(fmaf(s[kb][j], c, -lse2));
+                    if (need_mask && key > tcol) p = 0.f;
+                    s[kb][j] = p * (dp[kb][j] - Dr);
+                }
+            pv_block<D, KP>(ks, 0, s[0], dq, lane);
+            pv_block<D, KP>(ks, 32, s[1], dq, lane);
+        }
+        if (it + 1 < ntiles) sstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Depth rows of this wave's tokens: dQ^T += Kd^T dS_d^T.
+    if (L > 0) {
+        uint16_t* kslice = smem + w * 32 * KP;
+        const int64_t TL_rows = (int64_t)T * L;
+        const uint16_t* Kdb = a.Kd + kvbase * (int64_t)L * D;
+        const uint16_t* Vdb = a.Vd + kvbase * (int64_t)L * D;
+        const int64_t dlo = (int64_t)tw_lo * L, dhi = (int64_t)(tw_hi + 1) * L;
+        for (int64_t rb = dlo; rb < dhi; rb += 32) {
+#pragma unroll
+            for (int i = 0; i < D / 16; ++i) {
+                const int cc = lane + 64 * i, row = cc / CH, ch = cc % CH;
+                const int64_t r = min(rb + row, TL_rows - 1);
+                st16(kslice + row * KP + ch * 8, ld16(Kdb + r * D + ch * 8));
+            }
+            f32x16 s, dp;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) s[j] = dp[j] = 0.f;
+            {
+                const int64_t r = min(rb + col, TL_rows - 1);
+                const uint16_t* vrow = Vdb + r * D + 8 * hf;
+#pragma unroll
+                for (int si = 0; si < D / 16; ++si)
+                    dp = mfma32(__builtin_bit_cast(bf16x8, ld16(vrow + 16 * si)), dreg[si], dp);
+            }
+            wave_lds_sync();
+            {
+                const uint16_t* krow = kslice + col * KP + 8 * hf;
+#pragma unroll
+                for (int si = 0; si < D / 16; ++si)
+                    s = mfma32(*(const bf16x8*)(krow + 16 * si), qreg[si], s);
+            }
+            const int64_t lo = (int64_t)tcol * L - rb - 4 * hf;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int rj = (j >> 2) * 8 + (j & 3);
+                float p = fast_exp2(fmaf(s[j], c, -lse2));
+                if (rj < lo || rj >= lo + L) p = 0.f;
+                s[j] = p * (dp[j] - Dr);
+            }
+            pv_block<D, KP>(kslice, 0, s, dq, lane);
+            wave_lds_sync();
+        }
+    }
+    if (valid) store_row_bf16<D>(a.dQ + qrow_idx * D, dq, a.scale, lane);
+}
+
+// ---------------------------------------------------------------- bwd_dkdv
+constexpr int BQ = 64;  // folded query rows per staged tile (bwd_dkdv)
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
+{
+    constexpr int KP = D + 8;
+    constexpr int NT = NW * 64;
+    constexpr int CH = D / 8;
+    constexpr int LOADS = BQ * CH / NT;
+    static_assert(BQ * CH % NT == 0, "tile staging must divide evenly");
+    constexpr int BK = NW * 32;   // keys per workgroup
+    // [buf][Q, dO][BQ rows * KP] then [buf][lse2, D][BQ]
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * BQ * KP];
+    __shared__ __attribute__((aligned(16))) float srow[2][2][BQ];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int col = lane & 31, hf = lane >> 5;
+    const int G = a.G, T = a.T, lgG = a.lgG;
+
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int unit = logical / a.nblocks;
+    const int kblk = logical % a.nblocks;        // small key blocks see the most queries: first
+    const int b = unit / a.Hk, kv = unit % a.Hk;
+    const int k0 = kblk * BK, kw = k0 + 32 * w, key = kw + col;
+    const bool kvalid = key < T;
+    const int64_t kvbase = ((int64_t)b * a.Hk + kv) * T;
+
+    bf16x8 kreg[D / 16], vreg[D / 16];
+    {
+        const uint16_t* krow = a.K + (kvbase + key) * D + 8 * hf;
+        const uint16_t* vrow = a.V + (kvbase + key) * D + 8 * hf;
+#pragma unroll
+        for (int si = 0; si < D / 16; ++si) {
+            kreg[si] = __builtin_bit_cast(bf16x8, kvalid ? ld16(krow + 16 * si) : make_uint4(0, 0, 0, 0));
+            vreg[si] = __builtin_bit_cast(bf16x8, kvalid ? ld16(vrow + 16 * si) : make_uint4(0, 0, 0, 0));
+        }
+    }
+    f32x16 dk[D / 32], dv[D / 32];
+    zero(dk);
+    zero(dv);
+
+    const int64_t TG = (int64_t)T * G;
+    const int64_t f_start = (int64_t)min(k0, T) * G;   // first folded row that sees a key of this block
+    const int ntiles = (int)((TG - f_start + BQ - 1) / BQ);
+    const int64_t qhead0 = (int64_t)b * a.Hq + (int64_t)kv * G;
+
+    uint4 qst[LOADS], dst[LOADS];
+    float lst = 0.f, dvst = 0.f;
+    auto gload = [&](int tile) {
+        const int64_t f0 = f_start + (int64_t)tile * BQ;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int cc = tid + i * NT, row = cc / CH, ch = cc % CH;
+            const int64_t f = f0 + row;
+            if (f < TG) {
+                const int64_t qi = (qhead0 + (f & (G - 1))) * T + (f >> lgG);
+                qst[i] = ld16(a.Q + qi * D + ch * 8);
+                dst[i] = ld16(a.dO + qi * D + ch * 8);
+            } else {
+                qst[i] = make_uint4(0, 0, 0, 0);
+                dst[i] = make_uint4(0, 0, 0, 0);
+            }
+        }
+        if (tid < BQ) {
+            const int64_t f = f0 + tid;
+            if (f < TG) {
+                const int64_t qi = (qhead0 + (f & (G - 1))) * T + (f >> lgG);
+                lst = a.lse2[qi];
+                dvst = a.Dv[qi];
+            } else {
+                lst = INFINITY;
+                dvst = 0.f;
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+        uint16_t* qs = smem + (2 * buf) * BQ * KP;
+        uint16_t* ds = qs + BQ * KP;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int cc = tid + i * NT, row = cc / CH, ch = cc % CH;
+            st16(qs + row * KP + ch * 8, qst[i]);
+            st16(ds + row * KP + ch * 8, dst[i]);
+        }
+        if (tid < BQ) {
+            srow[buf][0][tid] = lst;
+            srow[buf][1][tid] = dvst;
+        }
+    };
+
+    const float c = a.c;
+    if (ntiles > 0) {
+        gload(0);
+        sstore(0);
+    }
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+        const int buf = it & 1;
+        if (it + 1 < ntiles) gload(it + 1);
+        const uint16_t* qs = smem + (2 * buf) * BQ * KP;
+        const uint16_t* ds = qs + BQ * KP;
+        const int64_t f0 = f_start + (int64_t)it * BQ;
+#pragma unroll
+        for (int qb = 0; qb < BQ / 32; ++qb) {
+            const int64_t fb = f0 + qb * 32;
+            const int64_t tb_hi = (fb + 31) >> lgG;       // last token of the block
+            if (tb_hi < kw || fb >= TG) continue;         // wave-uniform: nothing visible
+            f32x16 s, dp;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) s[j] = dp[j] = 0.f;
+            const uint16_t* qrow = qs + (qb * 32 + col) * KP + 8 * hf;
+            const uint16_t* drow = ds + (qb * 32 + col) * KP + 8 * hf;
+#pragma unroll
+            for (int si = 0; si < D / 16; ++si) {
+                s = mfma32(*(const bf16x8*)(qrow + 16 * si), kreg[si], s);
+                dp = mfma32(*(const bf16x8*)(drow + 16 * si), vreg[si], dp);
+            }
+            const bool need_mask = (fb >> lgG) < kw + 31;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int rbase = qb * 32 + jj * 8 + 4 * hf;
+                const float4 l4 = *(const float4*)&srow[buf][0][rbase];
+                const float4 d4 = *(const float4*)&srow[buf][1][rbase];
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 4 * jj + e;
+                    float p = fast_exp2(fmaf(s[j], c, -lv[e]));
+                    if (need_mask && ((fb + jj * 8 + 4 * hf + e) >> lgG) < key) p = 0.f;
+                    s[j] = p;
+                    dp[j] = p * (dp[j] - dvv[e]);
+                }
+            }
+            pv_block<D, KP>(ds, qb * 32, s, dv, lane);
+            pv_block<D, KP>(qs, qb * 32, dp, dk, lane);
+        }
+        if (it + 1 < ntiles) sstore(buf ^ 1);
+        __syncthreads();
+    }
+    if (kvalid) {
+        store_row_bf16<D>(a.dK + (kvbase + key) * D, dk, a.scale, lane);
+        store_row_bf16<D>(a.dV + (kvbase + key) * D, dv, 1.f, lane);
+    }
+}
+
+// ---------------------------------------------------------------- bwd_depth
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_depth_kernel(BwdArgs a)
+{
+    constexpr int KP = D + 8;
+    constexpr int CH = D / 8;
+    constexpr int BM = NW * 32;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NW][2][32 * KP];   // per wave: Q, dO rows
+    __shared__ __attribute__((aligned(16))) float srow[NW][2][32];            // per wave: lse2, D
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int col = lane & 31, hf = lane >> 5;
+    const int G = a.G, T = a.T, L = a.L, lgG = a.lgG;
+
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int unit = logical / a.nblocks;
+    const int chunk = logical % a.nblocks;
+    const int b = unit / a.Hk, kv = unit % a.Hk;
+    const int64_t TG = (int64_t)T * G;
+    const int64_t fw = (int64_t)chunk * BM + 32 * w;
+    if (fw >= TG) return;   // wave-uniform; no workgroup barrier below
+    const int tw_lo = (int)(fw >> lgG);
+    const int tw_hi = (int)min((fw + 31) >> lgG, (int64_t)T - 1);
+    const int64_t qhead0 = (int64_t)b * a.Hq + (int64_t)kv * G;
+    const int64_t kvbase = ((int64_t)b * a.Hk + kv) * T;
+
+    uint16_t* qs = smem[w][0];
+    uint16_t* ds = smem[w][1];
+    // This wave's 32 query rows (folded) into its slices, row-major.
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+        const int cc = lane + 64 * i, row = cc / CH, ch = cc % CH;
+        const int64_t f = fw + row;
+        uint4 qv = make_uint4(0, 0, 0, 0), dv4 = make_uint4(0, 0, 0, 0);
+        if (f < TG) {
+            const int64_t qi = (qhead0 + (f & (G - 1))) * T + (f >> lgG);
+            qv = ld16(a.Q + qi * D + ch * 8);
+            dv4 = ld16(a.dO + qi * D + ch * 8);
+        }
+        st16(qs + row * KP + ch * 8, qv);
+        st16(ds + row * KP + ch * 8, dv4);
+    }
+    if (lane < 32) {
+        const int64_t f = fw + lane;
+        float lv = INFINITY, dvv = 0.f;
+        if (f < TG) {
+            const int64_t qi = (qhead0 + (f & (G - 1))) * T + (f >> lgG);
+            lv = a.lse2[qi];
+            dvv = a.Dv[qi];
+        }
+        srow[w][0][lane] = lv;
+        srow[w][1][lane] = dvv;
+    }
+    wave_lds_sync();
+    // Query rows as MFMA A operands (lane row l%32, k = d 16*si + 8*hf .. +8).
+    bf16x8 qreg[D / 16], dreg[D / 16];
+#pragma unroll
+    for (int si = 0; si < D / 16; ++si) {
+        qreg[si] = *(const bf16x8*)(qs + col * KP + 16 * si + 8 * hf);
+        dreg[si] = *(const bf16x8*)(ds + col * KP + 16 * si + 8 * hf);
+    }
+    // Per-register row statistics: register j <-> query row (j/4)*8 + 4*hf + j%4.
+    float lr[16], dr[16];
+    int tr[16];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const float4 l4 = *(const float4*)&srow[w][0][jj * 8 + 4 * hf];
+        const float4 d4 = *(const float4*)&srow[w][1][jj * 8 + 4 * hf];
+        lr[4 * jj + 0] = l4.x; lr[4 * jj + 1] = l4.y; lr[4 * jj + 2] = l4.z; lr[4 * jj + 3] = l4.w;
+        dr[4 * jj + 0] = d4.x; dr[4 * jj + 1] = d4.y; dr[4 * jj + 2] = d4.z; dr[4 * jj + 3] = d4.w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tr[4 * jj + e] = (int)((fw + jj * 8 + 4 * hf + e) >> lgG);
+    }
+
+    const float c = a.c;
+    const int64_t TL_rows = (int64_t)T * L;
+    const uint16_t* Kdb = a.Kd + kvbase * (int64_t)L * D;
+    const uint16_t* Vdb = a.Vd + kvbase * (int64_t)L * D;
+    uint16_t* dKdb = a.dKd + kvbase * (int64_t)L * D;
+    uint16_t* dVdb = a.dVd + kvbase * (int64_t)L * D;
+    const int64_t dlo = (int64_t)tw_lo * L, dhi = (int64_t)(tw_hi + 1) * L;
+    for (int64_t rb = dlo; rb < dhi; rb += 32) {
+        const int64_t r = rb + col;                          // this lane's depth row
+        const int64_t rl = min(r, TL_rows - 1);
+        const int rtok = (int)(rl / L);
+        f32x16 s, dp;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s[j] = dp[j] = 0.f;
+        const uint16_t* krow = Kdb + rl * D + 8 * hf;
+        const uint16_t* vrow = Vdb + rl * D + 8 * hf;
+#pragma unroll
+        for (int si = 0; si < D / 16; ++si) {
+            s = mfma32(qreg[si], __builtin_bit_cast(bf16x8, ld16(krow + 16 * si)), s);
+            dp = mfma32(dreg[si], __builtin_bit_cast(bf16x8, ld16(vrow + 16 * si)), dp);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            float p = fast_exp2(fmaf(s[j], c, -lr[j]));
+            if (tr[j] != rtok || r >= dhi) p = 0.f;
+            s[j] = p;
+            dp[j] = p * (dp[j] - dr[j]);
+        }
+        f32x16 gv[D / 32], gk[D / 32];
+        zero(gv);
+        zero(gk);
+        pv_block<D, KP>(ds, 0, s, gv, lane);
+        pv_block<D, KP>(qs, 0, dp, gk, lane);
+        if (r < dhi) {
+            store_row_bf16<D>(dVdb + r * D, gv, 1.f, lane);
+            store_row_bf16<D>(dKdb + r * D, gk, a.scale, lane);
+        }
+    }
+}
+
+template <int D>
+hipError_t run(const Shape& s, BwdArgs a, hipStream_t st)
+{
+    const int nunits = (int)(s.B * s.Hk);
+    const int64_t TG = s.T * s.G;
+    {
+        constexpr int RPB = 256 / (D / 8);
+        hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((a.rows + RPB - 1) / RPB)),
+                           dim3(256), 0, st, a);
+    }
+    {
+        constexpr int NW = 8;
+        a.nblocks = (int)((TG + NW * 32 - 1) / (NW * 32));
+        hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3((unsigned)(nunits * a.nblocks)),
+                           dim3(NW * 64), 0, st, a);
+    }
+    {
+        constexpr int NW = 4;
+        a.nblocks = (int)((s.T + NW * 32 - 1) / (NW * 32));
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW>), dim3((unsigned)(nunits * a.nblocks)),
+                           dim3(NW * 64), 0, st, a);
+    }
+    if (s.L > 0) {
+        constexpr int NW = 4;
+        a.nblocks = (int)((TG + NW * 32 - 1) / (NW * 32));
+        hipLaunchKernelGGL((bwd_depth_kernel<D, NW>), dim3((unsigned)(nunits * a.nblocks)),
+                           dim3(NW * 64), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
 
 hipError_t launch_bwd_bf16(const Shape& s, const void* Q, const void* K, const void* V,
                            const void* Kd, const void* Vd, const void* O, const float* lse,
                            const void* dO, void* dQ, void* dK, void* dV, void* dKd, void* dVd,
                            float* ws, hipStream_t st)
 {
-    return launch_bwd_rows_bf16(s, Q, K, V, Kd, Vd, O, lse, dO, dQ, dK, dV, dKd, dVd, ws, st);
+    BwdArgs a;
+    a.Q = (const uint16_t*)Q;
+    a.K = (const uint16_t*)K;
+    a.V = (const uint16_t*)V;
+    a.Kd = (const uint16_t*)Kd;
+    a.Vd = (const uint16_t*)Vd;
+    a.O = (const uint16_t*)O;
+    a.lse = lse;
+    a.dO = (const uint16_t*)dO;
+    a.dQ = (uint16_t*)dQ;
+    a.dK = (uint16_t*)dK;
+    a.dV = (uint16_t*)dV;
+    a.dKd = (uint16_t*)dKd;
+    a.dVd = (uint16_t*)dVd;
+    a.rows = s.B * s.Hq * s.T;
+    a.lse2 = ws;
+    a.Dv = ws + a.rows;
+    a.Hq = (int)s.Hq;
+    a.Hk = (int)s.Hk;
+    a.T = (int)s.T;
+    a.L = (int)s.L;
+    a.G = s.G;
+    a.lgG = 0;
+    while ((1 << a.lgG) < s.G) ++a.lgG;
+    a.c = s.scale * kLog2e;
+    a.scale = s.scale;
+    a.nblocks = 1;
+    return s.d == 128 ? run<128>(s, a, st) : run<64>(s, a, st);
 }
 
 }  // namespace moda

@@ -59,6 +59,72 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float 
     return r;
 }
 
+// acc^T += X^T P for a block of 32 rows of X held in LDS rows [row0, row0+32)
+// of a row-major tile with pitch KP (X = V for the attention output, dO or Q
+// for gradients).  p holds the 32x32 block of weights in MFMA output layout
+// (lane column l%32, register j <-> row (j/4)*8 + 4*(l/32) + j%4).  X is read
+// transposed (ds_read_b64_tr_b16) so that k-slot e of lane half h is row
+// 16*sp + 8*(e/4) + 4*h + e%4, which is the row register 8*sp + e of p holds;
+// acc[db] receives rows d = 32*db + (j/4)*8 + 4*h + j%4 of column l%32.
+template <int D, int KP>
+__device__ __forceinline__ void pv_block(const uint16_t* x, int row0, const f32x16& p,
+                                         f32x16 (&acc)[D / 32], int lane)
+{
+    const int col = lane & 31, hf = lane >> 5;
+    const int krow = row0 + 4 * hf + ((col & 15) >> 2);   // + 16*sp + 8*q
+    const int dcol = 16 * (col >> 4) + 4 * (col & 3);      // + 32*db
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+        const bf16x8 pb = to_bf16x8(p[8 * sp + 0], p[8 * sp + 1], p[8 * sp + 2], p[8 * sp + 3],
+                                    p[8 * sp + 4], p[8 * sp + 5], p[8 * sp + 6], p[8 * sp + 7]);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const uint16_t* base = x + (krow + 16 * sp) * KP + dcol + 32 * db;
+            const bf16x4 lo = lds_read_tr(base);
+            const bf16x4 hi = lds_read_tr(base + 8 * KP);
+            const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            acc[db] = mfma32(a, pb, acc[db]);
+        }
+    }
+}
+
+// Store a D x 32 accumulator held as acc^T blocks (lane column l%32 owns one
+// output row) as bf16 row `row` of out, times `mul`: register j of block db is
+// element 32*db + (j/4)*8 + 4*(l/32) + j%4.
+template <int D>
+__device__ __forceinline__ void store_row_bf16(uint16_t* row, const f32x16 (&acc)[D / 32],
+                                               float mul, int lane)
+{
+    const int hf = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            bf16x4 v;
+            v[0] = (__bf16)(acc[db][4 * jj + 0] * mul);
+            v[1] = (__bf16)(acc[db][4 * jj + 1] * mul);
+            v[2] = (__bf16)(acc[db][4 * jj + 2] * mul);
+            v[3] = (__bf16)(acc[db][4 * jj + 3] * mul);
+            *(bf16x4*)(row + 32 * db + 8 * jj + 4 * hf) = v;
+        }
+}
+
+template <int N>
+__device__ __forceinline__ void zero(f32x16 (&a)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) a[i][j] = 0.f;
+}
+
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ uint4 ld16(const void* p) { return *(const uint4*)p; }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *(uint4*)p = v; }
 

@@ -88,32 +88,6 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[2], float& m, float& 
         for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
 }
 
-// O^T += V^T P^T for a block of 32 keys held in LDS rows [row0, row0+32) of a
-// row-major tile with pitch KP.  p holds the weights of those 32 keys
-// (S^T output layout); the V operand is read transposed so that k-slot e of
-// lane half h is key 16*sp + 8*(e/4) + 4*h + e%4, matching the P layout.
-template <int D, int KP>
-__device__ __forceinline__ void pv_block(const uint16_t* vt, int row0, const f32x16& p,
-                                         f32x16 (&o)[D / 32], int lane)
-{
-    const int col = lane & 31, hf = lane >> 5;
-    const int krow = row0 + 4 * hf + ((col & 15) >> 2);   // + 16*sp + 8*q
-    const int dcol = 16 * (col >> 4) + 4 * (col & 3);      // + 32*db
-#pragma unroll
-    for (int sp = 0; sp < 2; ++sp) {
-        const bf16x8 pb = to_bf16x8(p[8 * sp + 0], p[8 * sp + 1], p[8 * sp + 2], p[8 * sp + 3],
-                                    p[8 * sp + 4], p[8 * sp + 5], p[8 * sp + 6], p[8 * sp + 7]);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-            const uint16_t* base = vt + (krow + 16 * sp) * KP + dcol + 32 * db;
-            const bf16x4 lo = lds_read_tr(base);
-            const bf16x4 hi = lds_read_tr(base + 8 * KP);
-            const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            o[db] = mfma32(a, pb, o[db]);
-        }
-    }
-}
-
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(FwdArgs a)
 {

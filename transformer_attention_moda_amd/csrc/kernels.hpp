@@ -32,12 +32,6 @@ hipError_t launch_bwd_f32(const Shape& s, const float* Q, const float* K, const 
                           const float* dO, float* dQ, float* dK, float* dV, float* dKd,
                           float* dVd, float* ws, hipStream_t st);
 
-// bf16 backward through the wave-per-row kernels.
-hipError_t launch_bwd_rows_bf16(const Shape& s, const void* Q, const void* K, const void* V,
-                                const void* Kd, const void* Vd, const void* O, const float* lse,
-                                const void* dO, void* dQ, void* dK, void* dV, void* dKd,
-                                void* dVd, float* ws, hipStream_t st);
-
 // Depth packer: [L, B, Hk, T, row_bytes] -> [B, Hk, T*L, row_bytes].
 hipError_t launch_pack_depth(int64_t L, int64_t B, int64_t Hk, int64_t T, int64_t row_bytes,
                              const void* layers, void* packed, hipStream_t st);

@@ -1,4 +1,4 @@
-// Wave-per-row MoDA kernels: fp32 forward and backward, and a bf16 backward.
+// Wave-per-row MoDA kernels: the fp32 forward and backward.
 //
 // One wavefront handles one query row (forward), one token's G query rows
 // (dQ and the token's depth gradients) or one sequence key (dK, dV).  The 64
@@ -13,24 +13,8 @@
 namespace moda {
 namespace {
 
-template <typename T>
-__device__ __forceinline__ float ldf(const T* p, int64_t i);
-template <>
-__device__ __forceinline__ float ldf<float>(const float* p, int64_t i) { return p[i]; }
-template <>
-__device__ __forceinline__ float ldf<uint16_t>(const uint16_t* p, int64_t i)
-{
-    return __uint_as_float(((uint32_t)p[i]) << 16);
-}
-template <typename T>
-__device__ __forceinline__ void stf(T* p, int64_t i, float v);
-template <>
-__device__ __forceinline__ void stf<float>(float* p, int64_t i, float v) { p[i] = v; }
-template <>
-__device__ __forceinline__ void stf<uint16_t>(uint16_t* p, int64_t i, float v)
-{
-    p[i] = __builtin_bit_cast(uint16_t, (__bf16)v);
-}
+__device__ __forceinline__ float ldf(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ void stf(float* p, int64_t i, float v) { p[i] = v; }
 
 __device__ __forceinline__ float wave_sum(float x)
 {
@@ -302,17 +286,6 @@ hipError_t launch_bwd_f32(const Shape& s, const float* Q, const float* K, const 
     a.Q = Q; a.K = K; a.V = V; a.Kd = Kd; a.Vd = Vd; a.O = O; a.lse = lse; a.dO = dO;
     a.dQ = dQ; a.dK = dK; a.dV = dV; a.dKd = dKd; a.dVd = dVd; a.Dws = ws;
     return s.d == 128 ? run_bwd<float, 128>(a, st) : run_bwd<float, 64>(a, st);
-}
-
-hipError_t launch_bwd_rows_bf16(const Shape& s, const void* Q, const void* K, const void* V,
-                                const void* Kd, const void* Vd, const void* O, const float* lse,
-                                const void* dO, void* dQ, void* dK, void* dV, void* dKd,
-                                void* dVd, float* ws, hipStream_t st)
-{
-    RowArgs a = make_args(s);
-    a.Q = Q; a.K = K; a.V = V; a.Kd = Kd; a.Vd = Vd; a.O = O; a.lse = lse; a.dO = dO;
-    a.dQ = dQ; a.dK = dK; a.dV = dV; a.dKd = dKd; a.dVd = dVd; a.Dws = ws;
-    return s.d == 128 ? run_bwd<uint16_t, 128>(a, st) : run_bwd<uint16_t, 64>(a, st);
 }
 
 }  // namespace moda
