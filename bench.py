@@ -43,6 +43,9 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-l0", action="store_true", help="skip the L=0 comparison run")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device-to-device copy of this many MiB first (a "
+                         "kernel of known traffic for scaling hardware byte counters)")
     return ap.parse_args()
 
 
@@ -74,47 +77,97 @@ class Step:
             self.pp = binding.problem(B, Hk, Hk, T, d, L, 1.0, binding.MODA_BF16)
         self.events = []
 
-    def run(self, record=False):
-        torch, mb, x = self.torch, self.mb, self.x
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
-        if record:
-            ev[0].record()
+    def run(self):
+        mb, x = self.mb, self.x
         if self.L > 0:
             mb.moda_pack_depth(self.pp, x["layers_K"], self.Kd)
             mb.moda_pack_depth(self.pp, x["layers_V"], self.Vd)
-        if record:
-            ev[1].record()
         mb.moda_fwd(self.p, x["Q"], x["K"], x["V"], self.Kd, self.Vd, self.O, self.lse)
-        if record:
-            ev[2].record()
         mb.moda_bwd(self.p, x["Q"], x["K"], x["V"], self.Kd, self.Vd, self.O, self.lse, x["dO"],
                     self.dQ, self.dK, self.dV, self.dKd, self.dVd, self.ws)
-        if record:
-            ev[3].record()
-            self.events.append(ev)
 
     def timed(self, steps, warmup):
+        """Average step time (ms) over `steps`, and per kernel the average
+        duration (ms) and launches per step, from HIP events libmoda records
+        around each of its kernels on the stream they run on."""
         torch = self.torch
         for _ in range(warmup):
             self.run()
         torch.cuda.synchronize()
-        self.events = []
+        timer = self.mb.KernelTimer(capacity=16 * 2 * steps + 16)
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
+        timer.arm()
         wall0 = time.perf_counter()
         t0.record()
         for _ in range(steps):
-            self.run(record=True)
+            self.run()
         t1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
-        total_ms = t0.elapsed_time(t1)
-        parts = {"pack": 0.0, "fwd": 0.0, "bwd": 0.0}
-        for ev in self.events:
-            parts["pack"] += ev[0].elapsed_time(ev[1])
-            parts["fwd"] += ev[1].elapsed_time(ev[2])
-            parts["bwd"] += ev[2].elapsed_time(ev[3])
-        return total_ms / steps, {k: v / steps for k, v in parts.items()}, wall
+        results = timer.results()
+        timer.disarm()
+        kernels = {}
+        for label, ms in results:
+            k = kernels.setdefault(label, {"total_ms": 0.0, "launches": 0})
+            k["total_ms"] += ms
+            k["launches"] += 1
+        timer.close()
+        for k in kernels.values():
+            k["avg_ms"] = k["total_ms"] / k["launches"]
+            k["per_step"] = k["launches"] / steps
+        return t0.elapsed_time(t1) / steps, kernels, wall
+
+
+def traffic_for(label):
+    """Per-launch HBM traffic of a kernel from the committed rocprofv3 counter
+    summary (profiles/traffic.txt: FETCH_SIZE and WRITE_SIZE, each scaled by
+    the factor a plain copy of known size gives), or None when the kernel's
+    sources changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        f = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
+        if f.get("kernel") != label:
+            continue
+        h = hashlib.sha256()
+        for src in f.get("sources", "").split(","):
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        if h.hexdigest()[:16] != f.get("sha"):
+            return None
+        return {"fetch_bytes": float(f["fetch_bytes"]), "write_bytes": float(f["write_bytes"]),
+                "bytes": float(f["fetch_bytes"]) + float(f["write_bytes"])}
+    return None
+
+
+def kernel_work(label, w):
+    """Algorithmic work of one launch of a libmoda kernel: (bound, amount, unit).
+
+    Sequence pairs P_s = B Hq T(T+1)/2 and depth pairs P_d = B Hq T L are the
+    visible (query, key) pairs.  FLOP counts are 2 d per pair and product:
+    forward = S and O products over all pairs (4 d); backward = 5 products
+    (S recomputed, dP, dV, dK, dQ), of which bwd_dkdv does the four sequence
+    ones besides dQ, bwd_depth the four depth ones, bwd_dq the dQ product
+    (its own S and dP are recomputation).  Memory-bound kernels count the
+    bytes they must move once."""
+    d, B, Hq, Hk, T, L = w.d, w.B, w.Hq, w.Hk, w.T, w.L
+    Ps, Pd = B * Hq * T * (T + 1) / 2, B * Hq * T * L
+    q_bytes, dep_bytes, rows = B * Hq * T * d * 2, B * Hk * T * L * d * 2, B * Hq * T
+    if label == "fwd":
+        return "mfma", 4 * d * (Ps + Pd), "FLOP"
+    if label == "bwd_dkdv":
+        return "mfma", 8 * d * Ps, "FLOP"
+    if label == "bwd_dq":
+        return "mfma", 2 * d * (Ps + Pd), "FLOP"
+    if label == "bwd_depth":
+        return "hbm", 4 * dep_bytes + 2 * q_bytes + 8 * rows, "B"
+    if label == "bwd_pre":
+        return "hbm", 2 * q_bytes + 12 * rows, "B"
+    if label == "pack":
+        return "hbm", 2 * dep_bytes, "B"   # one of K or V per launch: read + write
+    return None, 0, None
 
 
 def cpu_baseline(w, step, seconds):
@@ -147,8 +200,12 @@ def cpu_baseline(w, step, seconds):
         return dt, 3.5 * 4.0 * d * pairs, t_lo
 
     sample(1)                      # start the OpenMP pool
-    dt, fl, _ = sample(8)
-    n = int(max(8, min(T, 8 * seconds / max(dt, 1e-3))))
+    n = 8
+    dt, fl, _ = sample(n)
+    while dt < seconds / 8 and n < T:   # grow the sample until it takes a measurable time
+        n = min(T, n * 4)
+        dt, fl, _ = sample(n)
+    n = int(max(n, min(T, n * seconds / max(dt, 1e-3))))
     dt, fl, t_lo = sample(n)
     return {
         "value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": th, "kind": "oracle",
@@ -171,9 +228,17 @@ def main():
     binding.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = inputs.WORKLOADS[args.workload]
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, device="cuda:0", dtype=torch.uint8).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     step = Step(w, w.L, seed=0)
-    ms, parts, wall = step.timed(args.steps, args.warmup)
+    ms, kernels, wall = step.timed(args.steps, args.warmup)
     f_fwd, f_all = fwd_flops(w), 3.5 * fwd_flops(w)
     value = f_all / (ms * 1e-3) / 1e12
 
@@ -182,27 +247,25 @@ def main():
         del step.x["layers_K"], step.x["layers_V"]
         torch.cuda.empty_cache()
         s0 = Step(w, 0, seed=0)
-        ms0, parts0, _ = s0.timed(args.steps, args.warmup)
-        res0 = {"ms_per_step": ms0, "fwd_ms": parts0["fwd"], "bwd_ms": parts0["bwd"]}
+        ms0, k0, _ = s0.timed(args.steps, args.warmup)
+        res0 = {"ms_per_step": ms0, "kernels": k0}
         del s0
         torch.cuda.empty_cache()
 
-    # Dominant kernel of the step and its roofline.
-    depth_bytes = 2 * w.B * w.Hk * w.T * w.L * w.d * 2
-    cand = {
-        "fwd": ("mfma", f_fwd / (parts["fwd"] * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"),
-        "bwd": ("mfma", 2.5 * f_fwd / (parts["bwd"] * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS,
-                "TFLOP/s"),
-        "pack": ("hbm", 2 * depth_bytes / (parts["pack"] * 1e-3) / 1e9 if parts["pack"] else 0,
-                 HBM_PEAK_GBS, "GB/s"),
-    }
-    dom = max(parts, key=parts.get)
-    bound, ach, peak, unit = cand[dom]
-    roof = {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
-            "frac": round(ach / peak, 4), "traffic": None, "kernel": f"moda_{dom}",
-            "per_entry_point": {k: {"ms": round(parts[k], 3), "achieved": round(cand[k][1], 2),
-                                    "unit": cand[k][3], "frac": round(cand[k][1] / cand[k][2], 4)}
-                                for k in parts}}
+    def roof(label, k, wl):
+        bound, amount, _ = kernel_work(label, wl)
+        if bound == "mfma":
+            ach, peak, unit = amount / (k["avg_ms"] * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+        else:
+            ach, peak, unit = amount / (k["avg_ms"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+        return {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                "frac": round(ach / peak, 4)}
+
+    dom = max(kernels, key=lambda n: kernels[n]["avg_ms"] * kernels[n]["per_step"])
+    roofline = dict(roof(dom, kernels[dom], w), traffic=traffic_for(dom), kernel=dom,
+                    avg_ms=round(kernels[dom]["avg_ms"], 4))
+    per_kernel = {n: dict(roof(n, k, w), avg_ms=round(k["avg_ms"], 4),
+                          launches_per_step=k["per_step"]) for n, k in kernels.items()}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -222,20 +285,28 @@ def main():
                    "L": w.L, "step": "pack depth K,V + forward + backward",
                    "chunk_tokens": binding.moda_fwd_chunk_tokens(step.p)},
         "pct_mfma_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
-        "fwd_tflops": round(f_fwd / (parts["fwd"] * 1e-3) / 1e12, 2),
-        "ms": {k: round(v, 3) for k, v in parts.items()},
-        "roofline": roof,
+        "roofline": roofline,
+        "fwd": {"ms": round(kernels["fwd"]["avg_ms"], 3),
+                "tflops": round(f_fwd / (kernels["fwd"]["avg_ms"] * 1e-3) / 1e12, 2),
+                "frac": round(f_fwd / (kernels["fwd"]["avg_ms"] * 1e-3) / 1e12 /
+                              MFMA_BF16_PEAK_TFLOPS, 4)},
+        "kernels": per_kernel,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }
     if res0:
-        out["l0"] = {k: round(v, 3) for k, v in res0.items()}
+        k0 = res0["kernels"]
+        fwd_l, fwd_0 = kernels["fwd"]["avg_ms"], k0["fwd"]["avg_ms"]
+        bwd_l = sum(v["avg_ms"] * v["per_step"] for n, v in kernels.items() if n.startswith("bwd"))
+        bwd_0 = sum(v["avg_ms"] * v["per_step"] for n, v in k0.items() if n.startswith("bwd"))
+        out["l0"] = {"ms_per_step": round(res0["ms_per_step"], 3), "fwd_ms": round(fwd_0, 3),
+                     "bwd_ms": round(bwd_0, 3),
+                     "fwd_tflops": round(fwd_flops(w, 0) / (fwd_0 * 1e-3) / 1e12, 2)}
         out["overhead"] = {
-            "fwd": round((parts["fwd"] - res0["fwd_ms"]) / res0["fwd_ms"], 4),
-            "fwd_bwd": round((parts["fwd"] + parts["bwd"] - res0["fwd_ms"] - res0["bwd_ms"]) /
-                             (res0["fwd_ms"] + res0["bwd_ms"]), 4),
+            "fwd": round((fwd_l - fwd_0) / fwd_0, 4),
+            "fwd_bwd": round((fwd_l + bwd_l - fwd_0 - bwd_0) / (fwd_0 + bwd_0), 4),
             "step": round((ms - res0["ms_per_step"]) / res0["ms_per_step"], 4),
-            "fwd_pages_convention": round((parts["fwd"] - res0["fwd_ms"]) / parts["fwd"], 4),
+            "fwd_pages_convention": round((fwd_l - fwd_0) / fwd_l, 4),
         }
     print(json.dumps(out), flush=True)
 

@@ -137,6 +137,24 @@ const char* moda_last_error(void);
  * for p, or 0 if p is invalid or unsupported. */
 int32_t moda_fwd_chunk_tokens(const moda_problem_t* p);
 
+/*
+ * Per-kernel timing hook (profiling support; not part of the operator).
+ * events: caller-created hipEvent_t handles (cast to void*), count >= 0.
+ * While armed, every kernel a libmoda entry point launches on this thread is
+ * bracketed by two of these events, recorded on the call's stream
+ * (events[2i] before and events[2i+1] after the i-th kernel since arming), as
+ * long as events remain; further kernels are not timed.  The events stay owned
+ * by the caller, who synchronises and reads them (hipEventElapsedTime).
+ * moda_timing_arm(NULL, 0) disarms.  Returns MODA_ERR_INVALID_ARGUMENT for a
+ * negative count or NULL events with count > 0.
+ */
+moda_status_t moda_timing_arm(void** events, int32_t count);
+
+/* Number of kernels bracketed since the last moda_timing_arm on this thread,
+ * and the name of the i-th of them (NULL if out of range). */
+int32_t moda_timing_count(void);
+const char* moda_timing_label(int32_t i);
+
 #ifdef __cplusplus
 }
 #endif

@@ -152,3 +152,14 @@ def test_binding_raises_moda_error():
     with pytest.raises(mb.ModaError) as e:
         mb._check(mb.MODA_ERR_INVALID_ARGUMENT)
     assert e.value.status == mb.MODA_ERR_INVALID_ARGUMENT
+
+
+def test_timing_hook_argument_checks():
+    lib = mb.load()
+    assert lib.moda_timing_arm(None, 4) == mb.MODA_ERR_INVALID_ARGUMENT
+    evs = (ctypes.c_void_p * 2)()
+    assert lib.moda_timing_arm(evs, -1) == mb.MODA_ERR_INVALID_ARGUMENT
+    assert lib.moda_timing_arm(None, 0) == mb.MODA_OK
+    assert lib.moda_timing_count() == 0
+    assert lib.moda_timing_label(0) is None
+    assert lib.moda_timing_label(-1) is None

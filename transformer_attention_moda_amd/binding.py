@@ -22,7 +22,8 @@ MODA_BF16, MODA_F32 = 0, 1
 MODA_MAX_L = 1024
 
 EXPORTS = ("moda_fwd", "moda_bwd", "moda_bwd_workspace_bytes", "moda_pack_depth",
-           "moda_status_string", "moda_last_error", "moda_fwd_chunk_tokens")
+           "moda_status_string", "moda_last_error", "moda_fwd_chunk_tokens", "moda_timing_arm",
+           "moda_timing_count", "moda_timing_label")
 
 
 class ModaError(RuntimeError):
@@ -64,6 +65,12 @@ def load(path: str = LIB_PATH):
         lib.moda_last_error.restype = ctypes.c_char_p
         lib.moda_fwd_chunk_tokens.argtypes = [PP]
         lib.moda_fwd_chunk_tokens.restype = ctypes.c_int32
+        lib.moda_timing_arm.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
+        lib.moda_timing_arm.restype = I
+        lib.moda_timing_count.argtypes = []
+        lib.moda_timing_count.restype = ctypes.c_int32
+        lib.moda_timing_label.argtypes = [ctypes.c_int32]
+        lib.moda_timing_label.restype = ctypes.c_char_p
         _lib = lib
     return _lib
 
@@ -128,6 +135,54 @@ def moda_pack_depth(p: Problem, layers, packed, stream=None) -> None:
 
 def moda_fwd_chunk_tokens(p: Problem) -> int:
     return int(load().moda_fwd_chunk_tokens(ctypes.byref(p)))
+
+
+class KernelTimer:
+    """Per-kernel HIP-event timing through moda_timing_arm.
+
+    Creates `capacity` hipEvent_t handles with the HIP runtime, arms libmoda
+    with them, and after a synchronisation returns (label, milliseconds) for
+    every kernel libmoda launched on this thread since arming."""
+
+    def __init__(self, capacity: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = (ctypes.c_void_p * capacity)()
+        for i in range(capacity):
+            ev = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.events[i] = ev.value
+        self.capacity = capacity
+
+    def arm(self):
+        _check(load().moda_timing_arm(self.events, self.capacity))
+
+    def disarm(self):
+        _check(load().moda_timing_arm(None, 0))
+
+    def results(self):
+        lib = load()
+        out = []
+        for i in range(lib.moda_timing_count()):
+            a, b = self.events[2 * i], self.events[2 * i + 1]
+            if self.hip.hipEventSynchronize(b) != 0:
+                raise RuntimeError("hipEventSynchronize failed")
+            ms = ctypes.c_float()
+            if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append((lib.moda_timing_label(i).decode(), ms.value))
+        return out
+
+    def close(self):
+        for e in self.events:
+            if e:
+                self.hip.hipEventDestroy(e)
+        self.events = None
 
 
 # ---- allocating conveniences (torch allocates; libmoda computes) ----

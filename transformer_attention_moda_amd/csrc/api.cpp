@@ -124,9 +124,57 @@ size_t bwd_ws_bytes(const moda::Shape& s)
     return (2 * rows * sizeof(float) + 255) & ~size_t(255);
 }
 
+struct Timing {
+    hipEvent_t* events = nullptr;
+    int32_t count = 0;
+    int32_t used = 0;   // events recorded
+    const char* labels[512];
+    int32_t nlabels = 0;
+};
+thread_local Timing g_timing;
+
 }  // namespace
 
+namespace moda {
+
+void timing_begin(const char* label, hipStream_t st)
+{
+    Timing& t = g_timing;
+    if (!t.events || t.used + 2 > t.count) return;
+    hipEventRecord(t.events[t.used++], st);
+    if (t.nlabels < 512) t.labels[t.nlabels++] = label;
+}
+
+void timing_end(hipStream_t st)
+{
+    Timing& t = g_timing;
+    if (!t.events || t.used % 2 == 0) return;
+    hipEventRecord(t.events[t.used++], st);
+}
+
+}  // namespace moda
+
 extern "C" {
+
+moda_status_t moda_timing_arm(void** events, int32_t count)
+{
+    if (count < 0 || (count > 0 && !events))
+        return fail(MODA_ERR_INVALID_ARGUMENT, "bad timing event array");
+    g_timing.events = count > 0 ? reinterpret_cast<hipEvent_t*>(events) : nullptr;
+    g_timing.count = count;
+    g_timing.used = 0;
+    g_timing.nlabels = 0;
+    return MODA_OK;
+}
+
+int32_t moda_timing_count(void) { return g_timing.used / 2; }
+
+const char* moda_timing_label(int32_t i)
+{
+    if (i < 0 || i >= g_timing.nlabels || i >= g_timing.used / 2) return nullptr;
+    return g_timing.labels[i];
+}
+
 
 const char* moda_status_string(moda_status_t s)
 {

@@ -515,26 +515,34 @@ hipError_t run(const Shape& s, BwdArgs a, hipStream_t st)
     const int64_t TG = s.T * s.G;
     {
         constexpr int RPB = 256 / (D / 8);
+        timing_begin("bwd_pre", st);
         hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((a.rows + RPB - 1) / RPB)),
                            dim3(256), 0, st, a);
+        timing_end(st);
     }
     {
         constexpr int NW = 8;
         a.nblocks = (int)((TG + NW * 32 - 1) / (NW * 32));
+        timing_begin("bwd_dq", st);
         hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3((unsigned)(nunits * a.nblocks)),
                            dim3(NW * 64), 0, st, a);
+        timing_end(st);
     }
     {
         constexpr int NW = 4;
         a.nblocks = (int)((s.T + NW * 32 - 1) / (NW * 32));
+        timing_begin("bwd_dkdv", st);
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW>), dim3((unsigned)(nunits * a.nblocks)),
                            dim3(NW * 64), 0, st, a);
+        timing_end(st);
     }
     if (s.L > 0) {
         constexpr int NW = 4;
         a.nblocks = (int)((TG + NW * 32 - 1) / (NW * 32));
+        timing_begin("bwd_depth", st);
         hipLaunchKernelGGL((bwd_depth_kernel<D, NW>), dim3((unsigned)(nunits * a.nblocks)),
                            dim3(NW * 64), 0, st, a);
+        timing_end(st);
     }
     return hipGetLastError();
 }

@@ -278,7 +278,9 @@ template <int D, int NW>
 hipError_t launch(const Shape& s, const FwdArgs& a, int nunits, hipStream_t st)
 {
     const int64_t grid = (int64_t)nunits * a.nchunks;
+    timing_begin("fwd", st);
     hipLaunchKernelGGL((fwd_bf16_kernel<D, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
+    timing_end(st);
     return hipGetLastError();
 }
 

@@ -7,6 +7,10 @@
 
 namespace moda {
 
+// Timing hook: bracket one kernel launch with the caller's events, if armed.
+void timing_begin(const char* label, hipStream_t st);
+void timing_end(hipStream_t st);
+
 struct Shape {
     int64_t B, Hq, Hk, T, d, L;
     float scale;

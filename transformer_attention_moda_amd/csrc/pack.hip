@@ -55,8 +55,10 @@ hipError_t launch_pack_depth(int64_t L, int64_t B, int64_t Hk, int64_t T, int64_
     const int64_t per_block = (int64_t)PACK_THREADS * PACK_UNROLL;
     int64_t blocks = (total + per_block - 1) / per_block;
     if (blocks > 256 * 64) blocks = 256 * 64;
+    timing_begin("pack", st);
     hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(PACK_THREADS), 0, st,
                        (const uint4*)layers, (uint4*)packed, L, B * Hk, T, cpr, total);
+    timing_end(st);
     return hipGetLastError();
 }
 

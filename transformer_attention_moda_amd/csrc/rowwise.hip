@@ -237,20 +237,28 @@ inline unsigned blocks_for(int64_t waves) { return (unsigned)((waves + WPB - 1) 
 template <typename E, int D>
 hipError_t run_fwd(const RowArgs& a, hipStream_t st)
 {
+    timing_begin("fwd_f32", st);
     hipLaunchKernelGGL((fwd_rows<E, D>), dim3(blocks_for((int64_t)a.B * a.Hq * a.T)),
                        dim3(WPB * 64), 0, st, a);
+    timing_end(st);
     return hipGetLastError();
 }
 
 template <typename E, int D>
 hipError_t run_bwd(const RowArgs& a, hipStream_t st)
 {
+    timing_begin("bwd_pre_f32", st);
     hipLaunchKernelGGL((bwd_pre<E, D>), dim3(blocks_for((int64_t)a.B * a.Hq * a.T)),
                        dim3(WPB * 64), 0, st, a);
+    timing_end(st);
+    timing_begin("bwd_token_f32", st);
     hipLaunchKernelGGL((bwd_token<E, D>), dim3(blocks_for((int64_t)a.B * a.Hk * a.T)),
                        dim3(WPB * 64), 0, st, a);
+    timing_end(st);
+    timing_begin("bwd_key_f32", st);
     hipLaunchKernelGGL((bwd_key<E, D>), dim3(blocks_for((int64_t)a.B * a.Hk * a.T)),
                        dim3(WPB * 64), 0, st, a);
+    timing_end(st);
     return hipGetLastError();
 }
 
