@@ -141,7 +141,7 @@ void timing_begin(const char* label, hipStream_t st)
 {
     Timing& t = g_timing;
     if (!t.events || t.used + 2 > t.count) return;
-    hipEventRecord(t.events[t.used++], st);
+    (void)hipEventRecord(t.events[t.used++], st);
     if (t.nlabels < 512) t.labels[t.nlabels++] = label;
 }
 
@@ -149,7 +149,7 @@ void timing_end(hipStream_t st)
 {
     Timing& t = g_timing;
     if (!t.events || t.used % 2 == 0) return;
-    hipEventRecord(t.events[t.used++], st);
+    (void)hipEventRecord(t.events[t.used++], st);
 }
 
 }  // namespace moda

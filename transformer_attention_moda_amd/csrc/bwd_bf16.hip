@@ -85,15 +85,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a)
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
 {
-    constexpr int KP = D + 8;
-    constexpr int ELEMS = BN * KP;
-    constexpr int NT = NW * 64;
-    constexpr int CH = D / 8;
-    constexpr int LOADS = BN * CH / NT;
-    static_assert(BN * CH % NT == 0, "tile staging must divide evenly");
+    using TL = LdsTile<D>;
+    constexpr int ELEMS = BN * TL::PITCH;
+    static_assert(BN % (TL::RPI * NW) == 0, "tile staging must divide evenly");
     constexpr int BM = NW * 32;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * ELEMS];
-    static_assert(NW * 32 * KP <= 2 * 2 * ELEMS, "depth slices must fit");
+    static_assert(NW * 32 * TL::PITCH <= 2 * 2 * ELEMS, "depth slices must fit");
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col = lane & 31, hf = lane >> 5;
@@ -136,38 +133,20 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
     zero(dq);
 
     const int ntiles = t_hi_wg / BN + 1;
-    uint4 kst[LOADS], vst[LOADS];
-    auto gload = [&](int tile) {
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int cc = tid + i * NT, row = cc / CH, ch = cc % CH;
-            const int key = tile * BN + row;
-            if (key < T) {
-                kst[i] = ld16(Kb + (int64_t)key * D + ch * 8);
-                vst[i] = ld16(Vb + (int64_t)key * D + ch * 8);
-            } else {
-                kst[i] = make_uint4(0, 0, 0, 0);
-                vst[i] = make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto sstore = [&](int buf) {
+    auto stage = [&](int tile, int buf) {
         uint16_t* ks = smem + (2 * buf) * ELEMS;
-        uint16_t* vs = ks + ELEMS;
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int cc = tid + i * NT, row = cc / CH, ch = cc % CH;
-            st16(ks + row * KP + ch * 8, kst[i]);
-            st16(vs + row * KP + ch * 8, vst[i]);
-        }
+        const int k0 = tile * BN;
+        stage_rows<D>(ks, BN, [&](int r) { return Kb + (int64_t)min(k0 + r, T - 1) * D; }, lane, w, NW);
+        stage_rows<D>(ks + ELEMS, BN, [&](int r) { return Vb + (int64_t)min(k0 + r, T - 1) * D; },
+                      lane, w, NW);
     };
 
-    gload(0);
-    sstore(0);
+    stage(0, 0);
+    wait_vmem();
     __syncthreads();
     for (int it = 0; it < ntiles; ++it) {
         const int buf = it & 1;
-        if (it + 1 < ntiles) gload(it + 1);
+        if (it + 1 < ntiles) stage(it + 1, buf ^ 1);
         const int k0 = it * BN;
         if (k0 <= tw_hi) {
             const uint16_t* ks = smem + (2 * buf) * ELEMS;
@@ -177,12 +156,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) s[kb][j] = dp[kb][j] = 0.f;
-                const uint16_t* krow = ks + (kb * 32 + col) * KP + 8 * hf;
-                const uint16_t* vrow = vs + (kb * 32 + col) * KP + 8 * hf;
 #pragma unroll
                 for (int si = 0; si < D / 16; ++si) {
-                    s[kb] = mfma32(*(const bf16x8*)(krow + 16 * si), qreg[si], s[kb]);
-                    dp[kb] = mfma32(*(const bf16x8*)(vrow + 16 * si), dreg[si], dp[kb]);
+                    s[kb] = mfma32(lds_chunk<D>(ks, kb * 32 + col, 16 * si + 8 * hf), qreg[si], s[kb]);
+                    dp[kb] = mfma32(lds_chunk<D>(vs, kb * 32 + col, 16 * si + 8 * hf), dreg[si], dp[kb]);
                 }
             }
             const bool need_mask = k0 + BN - 1 > tw_lo;
@@ -195,27 +172,23 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
                     if (need_mask && key > tcol) p = 0.f;
                     s[kb][j] = p * (dp[kb][j] - Dr);
                 }
-            pv_block<D, KP>(ks, 0, s[0], dq, lane);
-            pv_block<D, KP>(ks, 32, s[1], dq, lane);
+            pv_block<D>(ks, 0, s[0], dq, lane);
+            pv_block<D>(ks, 32, s[1], dq, lane);
         }
-        if (it + 1 < ntiles) sstore(buf ^ 1);
+        wait_vmem();
         __syncthreads();
     }
 
     // Depth rows of this wave's tokens: dQ^T += Kd^T dS_d^T.
     if (L > 0) {
-        uint16_t* kslice = smem + w * 32 * KP;
+        uint16_t* kslice = smem + w * 32 * TL::PITCH;
         const int64_t TL_rows = (int64_t)T * L;
         const uint16_t* Kdb = a.Kd + kvbase * (int64_t)L * D;
         const uint16_t* Vdb = a.Vd + kvbase * (int64_t)L * D;
         const int64_t dlo = (int64_t)tw_lo * L, dhi = (int64_t)(tw_hi + 1) * L;
         for (int64_t rb = dlo; rb < dhi; rb += 32) {
-#pragma unroll
-            for (int i = 0; i < D / 16; ++i) {
-                const int cc = lane + 64 * i, row = cc / CH, ch = cc % CH;
-                const int64_t r = min(rb + row, TL_rows - 1);
-                st16(kslice + row * KP + ch * 8, ld16(Kdb + r * D + ch * 8));
-            }
+            stage_rows<D>(kslice, 32, [&](int r) { return Kdb + min(rb + r, TL_rows - 1) * D; },
+                          lane, 0, 1);
             f32x16 s, dp;
 #pragma unroll
             for (int j = 0; j < 16; ++j) s[j] = dp[j] = 0.f;
@@ -226,13 +199,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
                 for (int si = 0; si < D / 16; ++si)
                     dp = mfma32(__builtin_bit_cast(bf16x8, ld16(vrow + 16 * si)), dreg[si], dp);
             }
+            wait_vmem();
             wave_lds_sync();
-            {
-                const uint16_t* krow = kslice + col * KP + 8 * hf;
 #pragma unroll
-                for (int si = 0; si < D / 16; ++si)
-                    s = mfma32(*(const bf16x8*)(krow + 16 * si), qreg[si], s);
-            }
+            for (int si = 0; si < D / 16; ++si)
+                s = mfma32(lds_chunk<D>(kslice, col, 16 * si + 8 * hf), qreg[si], s);
             const int64_t lo = (int64_t)tcol * L - rb - 4 * hf;
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
@@ -241,7 +212,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
                 if (rj < lo || rj >= lo + L) p = 0.f;
                 s[j] = p * (dp[j] - Dr);
             }
-            pv_block<D, KP>(kslice, 0, s, dq, lane);
+            pv_block<D>(kslice, 0, s, dq, lane);
             wave_lds_sync();
         }
     }
@@ -254,13 +225,11 @@ constexpr int BQ = 64;  // folded query rows per staged tile (bwd_dkdv)
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
 {
-    constexpr int KP = D + 8;
-    constexpr int NT = NW * 64;
-    constexpr int CH = D / 8;
-    constexpr int LOADS = BQ * CH / NT;
-    static_assert(BQ * CH % NT == 0, "tile staging must divide evenly");
+    using TL = LdsTile<D>;
+    constexpr int KP = TL::PITCH;
+    static_assert(BQ % (TL::RPI * NW) == 0, "tile staging must divide evenly");
     constexpr int BK = NW * 32;   // keys per workgroup
-    // [buf][Q, dO][BQ rows * KP] then [buf][lse2, D][BQ]
+    // [buf][Q, dO][BQ rows] then [buf][lse2, D][BQ]
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * BQ * KP];
     __shared__ __attribute__((aligned(16))) float srow[2][2][BQ];
 
@@ -295,44 +264,27 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
     const int ntiles = (int)((TG - f_start + BQ - 1) / BQ);
     const int64_t qhead0 = (int64_t)b * a.Hq + (int64_t)kv * G;
 
-    uint4 qst[LOADS], dst[LOADS];
+    // Query tile `tile` (folded rows f0 .. f0+BQ-1) into buffer `buf`: Q and dO rows by direct
+    // loads (rows past the end repeat the last row; their lse is +inf so their weights are 0),
+    // lse2 and D through registers by the first BQ threads.
     float lst = 0.f, dvst = 0.f;
-    auto gload = [&](int tile) {
+    auto qi_of = [&](int64_t f) {
+        f = min(f, TG - 1);
+        return (qhead0 + (f & (G - 1))) * T + (f >> lgG);
+    };
+    auto stage = [&](int tile, int buf) {
         const int64_t f0 = f_start + (int64_t)tile * BQ;
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int cc = tid + i * NT, row = cc / CH, ch = cc % CH;
-            const int64_t f = f0 + row;
-            if (f < TG) {
-                const int64_t qi = (qhead0 + (f & (G - 1))) * T + (f >> lgG);
-                qst[i] = ld16(a.Q + qi * D + ch * 8);
-                dst[i] = ld16(a.dO + qi * D + ch * 8);
-            } else {
-                qst[i] = make_uint4(0, 0, 0, 0);
-                dst[i] = make_uint4(0, 0, 0, 0);
-            }
-        }
+        uint16_t* qs = smem + (2 * buf) * BQ * KP;
+        stage_rows<D>(qs, BQ, [&](int r) { return a.Q + qi_of(f0 + r) * D; }, lane, w, NW);
+        stage_rows<D>(qs + BQ * KP, BQ, [&](int r) { return a.dO + qi_of(f0 + r) * D; }, lane, w,
+                      NW);
         if (tid < BQ) {
             const int64_t f = f0 + tid;
-            if (f < TG) {
-                const int64_t qi = (qhead0 + (f & (G - 1))) * T + (f >> lgG);
-                lst = a.lse2[qi];
-                dvst = a.Dv[qi];
-            } else {
-                lst = INFINITY;
-                dvst = 0.f;
-            }
+            lst = f < TG ? a.lse2[qi_of(f)] : INFINITY;
+            dvst = f < TG ? a.Dv[qi_of(f)] : 0.f;
         }
     };
-    auto sstore = [&](int buf) {
-        uint16_t* qs = smem + (2 * buf) * BQ * KP;
-        uint16_t* ds = qs + BQ * KP;
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int cc = tid + i * NT, row = cc / CH, ch = cc % CH;
-            st16(qs + row * KP + ch * 8, qst[i]);
-            st16(ds + row * KP + ch * 8, dst[i]);
-        }
+    auto sstore_rows = [&](int buf) {
         if (tid < BQ) {
             srow[buf][0][tid] = lst;
             srow[buf][1][tid] = dvst;
@@ -341,13 +293,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
 
     const float c = a.c;
     if (ntiles > 0) {
-        gload(0);
-        sstore(0);
+        stage(0, 0);
+        sstore_rows(0);
     }
+    wait_vmem();
     __syncthreads();
     for (int it = 0; it < ntiles; ++it) {
         const int buf = it & 1;
-        if (it + 1 < ntiles) gload(it + 1);
+        if (it + 1 < ntiles) stage(it + 1, buf ^ 1);
         const uint16_t* qs = smem + (2 * buf) * BQ * KP;
         const uint16_t* ds = qs + BQ * KP;
         const int64_t f0 = f_start + (int64_t)it * BQ;
@@ -359,12 +312,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
             f32x16 s, dp;
 #pragma unroll
             for (int j = 0; j < 16; ++j) s[j] = dp[j] = 0.f;
-            const uint16_t* qrow = qs + (qb * 32 + col) * KP + 8 * hf;
-            const uint16_t* drow = ds + (qb * 32 + col) * KP + 8 * hf;
 #pragma unroll
             for (int si = 0; si < D / 16; ++si) {
-                s = mfma32(*(const bf16x8*)(qrow + 16 * si), kreg[si], s);
-                dp = mfma32(*(const bf16x8*)(drow + 16 * si), vreg[si], dp);
+                s = mfma32(lds_chunk<D>(qs, qb * 32 + col, 16 * si + 8 * hf), kreg[si], s);
+                dp = mfma32(lds_chunk<D>(ds, qb * 32 + col, 16 * si + 8 * hf), vreg[si], dp);
             }
             const bool need_mask = (fb >> lgG) < kw + 31;
 #pragma unroll
@@ -382,10 +333,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
                     dp[j] = p * (dp[j] - dvv[e]);
                 }
             }
-            pv_block<D, KP>(ds, qb * 32, s, dv, lane);
-            pv_block<D, KP>(qs, qb * 32, dp, dk, lane);
+            pv_block<D>(ds, qb * 32, s, dv, lane);
+            pv_block<D>(qs, qb * 32, dp, dk, lane);
         }
-        if (it + 1 < ntiles) sstore(buf ^ 1);
+        if (it + 1 < ntiles) sstore_rows(buf ^ 1);
+        wait_vmem();
         __syncthreads();
     }
     if (kvalid) {
@@ -398,10 +350,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_depth_kernel(BwdArgs a)
 {
-    constexpr int KP = D + 8;
-    constexpr int CH = D / 8;
+    using TL = LdsTile<D>;
     constexpr int BM = NW * 32;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[NW][2][32 * KP];   // per wave: Q, dO rows
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NW][2][32 * TL::PITCH];   // per wave: Q, dO rows
     __shared__ __attribute__((aligned(16))) float srow[NW][2][32];            // per wave: lse2, D
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -422,20 +373,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_depth_kernel(BwdArgs a)
 
     uint16_t* qs = smem[w][0];
     uint16_t* ds = smem[w][1];
-    // This wave's 32 query rows (folded) into its slices, row-major.
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) {
-        const int cc = lane + 64 * i, row = cc / CH, ch = cc % CH;
-        const int64_t f = fw + row;
-        uint4 qv = make_uint4(0, 0, 0, 0), dv4 = make_uint4(0, 0, 0, 0);
-        if (f < TG) {
-            const int64_t qi = (qhead0 + (f & (G - 1))) * T + (f >> lgG);
-            qv = ld16(a.Q + qi * D + ch * 8);
-            dv4 = ld16(a.dO + qi * D + ch * 8);
-        }
-        st16(qs + row * KP + ch * 8, qv);
-        st16(ds + row * KP + ch * 8, dv4);
-    }
+    // This wave's 32 query rows (folded) into its slices; rows past the end repeat the last
+    // row, and their lse of +inf gives them zero weight.
+    auto qi_of = [&](int64_t f) {
+        f = min(f, TG - 1);
+        return (qhead0 + (f & (G - 1))) * T + (f >> lgG);
+    };
+    stage_rows<D>(qs, 32, [&](int r) { return a.Q + qi_of(fw + r) * D; }, lane, 0, 1);
+    stage_rows<D>(ds, 32, [&](int r) { return a.dO + qi_of(fw + r) * D; }, lane, 0, 1);
     if (lane < 32) {
         const int64_t f = fw + lane;
         float lv = INFINITY, dvv = 0.f;
@@ -447,13 +392,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_depth_kernel(BwdArgs a)
         srow[w][0][lane] = lv;
         srow[w][1][lane] = dvv;
     }
+    wait_vmem();
     wave_lds_sync();
     // Query rows as MFMA A operands (lane row l%32, k = d 16*si + 8*hf .. +8).
     bf16x8 qreg[D / 16], dreg[D / 16];
 #pragma unroll
     for (int si = 0; si < D / 16; ++si) {
-        qreg[si] = *(const bf16x8*)(qs + col * KP + 16 * si + 8 * hf);
-        dreg[si] = *(const bf16x8*)(ds + col * KP + 16 * si + 8 * hf);
+        qreg[si] = lds_chunk<D>(qs, col, 16 * si + 8 * hf);
+        dreg[si] = lds_chunk<D>(ds, col, 16 * si + 8 * hf);
     }
     // Per-register row statistics: register j <-> query row (j/4)*8 + 4*hf + j%4.
     float lr[16], dr[16];
@@ -499,8 +445,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_depth_kernel(BwdArgs a)
         f32x16 gv[D / 32], gk[D / 32];
         zero(gv);
         zero(gk);
-        pv_block<D, KP>(ds, 0, s, gv, lane);
-        pv_block<D, KP>(qs, 0, dp, gk, lane);
+        pv_block<D>(ds, 0, s, gv, lane);
+        pv_block<D>(qs, 0, dp, gk, lane);
         if (r < dhi) {
             store_row_bf16<D>(dVdb + r * D, gv, 1.f, lane);
             store_row_bf16<D>(dKdb + r * D, gk, a.scale, lane);

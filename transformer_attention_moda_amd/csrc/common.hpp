@@ -59,14 +59,67 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float 
     return r;
 }
 
+// Row-major LDS tile of D-element bf16 rows, unpadded, with the 16-byte chunks
+// of each row permuted: logical chunk c of row r sits at chunk c ^ swz(r).
+//  D = 128 (a row is the 64 banks once): swz(r) = 4*(r%4) + (r/4)%4.
+//  D = 64 (two rows per bank sweep):       swz(r) = 4*((r/2)%2) + (r/4)%4.
+// In both, a 16-byte MFMA operand read of one chunk across 16 consecutive rows
+// touches every bank once, and the 8 rows x 64 bytes of one transposed read
+// (rows 8i..8i+7, chunks 4j..4j+3) cover every bank exactly twice, the minimum
+// for 512 bytes.  Rows are whole 1 KiB blocks of 4 (D=128) or 8 (D=64) rows for
+// the direct global->LDS loads below.
+template <int D>
+struct LdsTile {
+    static_assert(D == 128 || D == 64, "head dimension");
+    static constexpr int PITCH = D;                 // elements per row
+    static constexpr int CPR = D / 8;               // 16-byte chunks per row
+    static constexpr int RPI = 1024 / (2 * D);      // rows per 1 KiB wave load
+    __device__ static __forceinline__ int swz(int row)
+    {
+        return D == 128 ? 4 * (row & 3) + ((row >> 2) & 3) : 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+    }
+    __device__ static __forceinline__ int off(int row, int elem)
+    {
+        return row * D + ((((elem >> 3) ^ swz(row))) << 3) + (elem & 7);
+    }
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glob_void_t;
+
+// Stage rows [0, nrows) of an LdsTile<D> with direct 16-byte global->LDS loads
+// (global_load_lds_dwordx4: lane i of a wave writes bytes [16i, 16i+16) of a
+// 1 KiB block).  Each wave instruction fills RPI rows; lane i fetches the
+// logical chunk that belongs at physical chunk i % CPR of its row.  rowptr(r)
+// returns the global address of tile row r (always a valid row).  Waves
+// w, w + nw, ... share the instructions.  The data is in LDS once the issuing
+// wave has waited for its vector-memory counter.
+template <int D, typename RowPtr>
+__device__ __forceinline__ void stage_rows(uint16_t* tile, int nrows, RowPtr rowptr, int lane,
+                                           int w, int nw)
+{
+    using TL = LdsTile<D>;
+    const int ninstr = nrows / TL::RPI;
+    const int rsub = lane / TL::CPR, p = lane % TL::CPR;
+    for (int k = w; k < ninstr; k += nw) {
+        const int r = k * TL::RPI + rsub;
+        const int c = p ^ TL::swz(r);
+        const uint16_t* g = rowptr(r) + c * 8;
+        __builtin_amdgcn_global_load_lds((glob_void_t*)g, (lds_void_t*)(tile + k * TL::RPI * D),
+                                         16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // acc^T += X^T P for a block of 32 rows of X held in LDS rows [row0, row0+32)
-// of a row-major tile with pitch KP (X = V for the attention output, dO or Q
-// for gradients).  p holds the 32x32 block of weights in MFMA output layout
-// (lane column l%32, register j <-> row (j/4)*8 + 4*(l/32) + j%4).  X is read
-// transposed (ds_read_b64_tr_b16) so that k-slot e of lane half h is row
+// of an LdsTile (X = V for the attention output, dO or Q for gradients).  p
+// holds the 32x32 block of weights in MFMA output layout (lane column l%32,
+// register j <-> row (j/4)*8 + 4*(l/32) + j%4).  X is read transposed
+// (ds_read_b64_tr_b16) so that k-slot e of lane half h is row
 // 16*sp + 8*(e/4) + 4*h + e%4, which is the row register 8*sp + e of p holds;
 // acc[db] receives rows d = 32*db + (j/4)*8 + 4*h + j%4 of column l%32.
-template <int D, int KP>
+template <int D>
 __device__ __forceinline__ void pv_block(const uint16_t* x, int row0, const f32x16& p,
                                          f32x16 (&acc)[D / 32], int lane)
 {
@@ -79,13 +132,19 @@ __device__ __forceinline__ void pv_block(const uint16_t* x, int row0, const f32x
                                     p[8 * sp + 4], p[8 * sp + 5], p[8 * sp + 6], p[8 * sp + 7]);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-            const uint16_t* base = x + (krow + 16 * sp) * KP + dcol + 32 * db;
-            const bf16x4 lo = lds_read_tr(base);
-            const bf16x4 hi = lds_read_tr(base + 8 * KP);
+            const bf16x4 lo = lds_read_tr(x + LdsTile<D>::off(krow + 16 * sp, dcol + 32 * db));
+            const bf16x4 hi = lds_read_tr(x + LdsTile<D>::off(krow + 16 * sp + 8, dcol + 32 * db));
             const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             acc[db] = mfma32(a, pb, acc[db]);
         }
     }
+}
+
+// The 16-byte MFMA operand chunk (elements 8*c .. 8*c+7) of row `row`.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_chunk(const uint16_t* tile, int row, int elem)
+{
+    return *(const bf16x8*)(tile + LdsTile<D>::off(row, elem));
 }
 
 // Store a D x 32 accumulator held as acc^T blocks (lane column l%32 owns one

@@ -48,15 +48,17 @@ struct FwdArgs {
 
 constexpr int BN = 64;  // keys per sequence tile
 
-template <int D>
-struct Tile {
-    static constexpr int KP = D + 8;  // LDS row pitch (elements): rows start 16 bytes apart in bank space
-    static constexpr int ELEMS = BN * KP;
-};
+// Sequence tiles beyond this threshold of max growth (log2 units) trigger a
+// rescale of the running output and sum; below it the stale max is kept and the
+// weights stay below 2^8, exactly representable in the same way.
+constexpr float kRescaleLog2 = 8.f;
 
 // Online-softmax update of one lane's column with the scores held in s[0..NB-1]
-// (raw q.k values, 16 per block; masked entries are -inf).  On return s holds
-// the weights exp2(c*(score - m_new)) and o/l are rescaled.
+// (raw q.k values, 16 per block; masked entries are -inf).  The running max m
+// is raised (and o, l rescaled by 2^(c(m - m_new))) only when some lane of the
+// wave would otherwise see a weight above 2^kRescaleLog2; o/l = softmax output
+// holds for any m, so keeping a stale m is exact.  On return s holds the
+// weights exp2(c*(score - m)).
 template <int D, int NB>
 __device__ __forceinline__ void softmax_update(f32x16 (&s)[2], float& m, float& l,
                                                f32x16 (&o)[D / 32], float c)
@@ -67,9 +69,18 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[2], float& m, float& 
 #pragma unroll
         for (int j = 0; j < 16; ++j) mt = fmaxf(mt, s[kb][j]);
     mt = max_halves(mt);
-    const float m_new = fmaxf(m, mt);
-    const float alpha = fast_exp2((m - m_new) * c);
-    const float mc = m_new * c;
+    const bool grow = (mt - m) * c > kRescaleLog2;   // true when m is still -inf
+    if (__any(grow)) {
+        const float m_new = fmaxf(m, mt);
+        const float alpha = fast_exp2((m - m_new) * c);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+        m = m_new;
+    }
+    const float mc = m * c;
     float ps = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
@@ -79,28 +90,19 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[2], float& m, float& 
             s[kb][j] = p;
             ps += p;
         }
-    ps = sum_halves(ps);
-    l = l * alpha + ps;
-    m = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+    l += sum_halves(ps);
 }
 
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(FwdArgs a)
 {
-    using TL = Tile<D>;
-    constexpr int KP = TL::KP;
-    constexpr int NT = NW * 64;
-    constexpr int CH = D / 8;                  // 16-byte chunks per row
-    constexpr int LOADS = BN * CH / NT;        // per thread, per tensor, per tile
-    static_assert(BN * CH % NT == 0, "tile staging must divide evenly");
+    using TL = LdsTile<D>;
+    constexpr int ELEMS = BN * TL::PITCH;      // one K or V tile
+    static_assert(BN % (TL::RPI * NW) == 0, "tile staging must divide evenly");
     constexpr int BM = NW * 32;
-    // [buf][K or V][BN rows * KP]; the depth phase reuses it as NW private 32-row slices.
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TL::ELEMS];
-    static_assert(NW * 32 * KP <= 2 * 2 * TL::ELEMS, "depth slices must fit");
+    // [buf][K or V][BN rows]; the depth phase reuses it as NW private 32-row slices.
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * ELEMS];
+    static_assert(NW * 32 * TL::PITCH <= 2 * 2 * ELEMS, "depth slices must fit");
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col = lane & 31, hf = lane >> 5;
@@ -146,53 +148,34 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(FwdArgs a)
 
     // ---- sequence phase ----
     const int ntiles = t_hi_wg / BN + 1;
-    uint4 kst[LOADS], vst[LOADS];
-    auto gload = [&](int tile) {
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int c = tid + i * NT, row = c / CH, ch = c % CH;
-            const int key = tile * BN + row;
-            if (key < T) {
-                kst[i] = ld16(Kb + (int64_t)key * D + ch * 8);
-                vst[i] = ld16(Vb + (int64_t)key * D + ch * 8);
-            } else {
-                kst[i] = make_uint4(0, 0, 0, 0);
-                vst[i] = make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto sstore = [&](int buf) {
-        uint16_t* ks = smem + (2 * buf) * TL::ELEMS;
-        uint16_t* vs = ks + TL::ELEMS;
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int c = tid + i * NT, row = c / CH, ch = c % CH;
-            st16(ks + row * KP + ch * 8, kst[i]);
-            st16(vs + row * KP + ch * 8, vst[i]);
-        }
+    // K and V tile `tile` into buffer `buf` (direct global->LDS; rows past T repeat row T-1,
+    // whose weights are masked to zero).
+    auto stage = [&](int tile, int buf) {
+        uint16_t* ks = smem + (2 * buf) * ELEMS;
+        const int k0 = tile * BN;
+        stage_rows<D>(ks, BN, [&](int r) { return Kb + (int64_t)min(k0 + r, T - 1) * D; }, lane, w, NW);
+        stage_rows<D>(ks + ELEMS, BN, [&](int r) { return Vb + (int64_t)min(k0 + r, T - 1) * D; },
+                      lane, w, NW);
     };
 
-    gload(0);
-    sstore(0);
+    stage(0, 0);
+    wait_vmem();
     __syncthreads();
     for (int it = 0; it < ntiles; ++it) {
         const int buf = it & 1;
-        if (it + 1 < ntiles) gload(it + 1);
+        if (it + 1 < ntiles) stage(it + 1, buf ^ 1);
         const int k0 = it * BN;
         if (k0 <= tw_hi) {
-            const uint16_t* ks = smem + (2 * buf) * TL::ELEMS;
-            const uint16_t* vs = ks + TL::ELEMS;
+            const uint16_t* ks = smem + (2 * buf) * ELEMS;
+            const uint16_t* vs = ks + ELEMS;
             f32x16 s[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
-                const uint16_t* krow = ks + (kb * 32 + col) * KP + 8 * hf;
 #pragma unroll
-                for (int si = 0; si < D / 16; ++si) {
-                    const bf16x8 av = *(const bf16x8*)(krow + 16 * si);
-                    s[kb] = mfma32(av, qreg[si], s[kb]);
-                }
+                for (int si = 0; si < D / 16; ++si)
+                    s[kb] = mfma32(lds_chunk<D>(ks, kb * 32 + col, 16 * si + 8 * hf), qreg[si], s[kb]);
             }
             if (k0 + BN - 1 > tw_lo) {   // tile reaches past the wave's first token: causal mask
 #pragma unroll
@@ -204,28 +187,24 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(FwdArgs a)
                     }
             }
             softmax_update<D, 2>(s, m, l, o, a.c);
-            pv_block<D, KP>(vs, 0, s[0], o, lane);
-            pv_block<D, KP>(vs, 32, s[1], o, lane);
+            pv_block<D>(vs, 0, s[0], o, lane);
+            pv_block<D>(vs, 32, s[1], o, lane);
         }
-        if (it + 1 < ntiles) sstore(buf ^ 1);
+        wait_vmem();
         __syncthreads();
     }
 
     // ---- depth phase: this wave's tokens only ----
     if (L > 0) {
-        uint16_t* vslice = smem + w * 32 * KP;   // private 32-row slice of the (now idle) tiles
+        uint16_t* vslice = smem + w * 32 * TL::PITCH;   // private 32-row slice of the idle tiles
         const int64_t TL_rows = (int64_t)T * L;
         const uint16_t* Kdb = a.Kd + kvbase * (int64_t)L * D;
         const uint16_t* Vdb = a.Vd + kvbase * (int64_t)L * D;
         const int64_t dlo = (int64_t)tw_lo * L, dhi = (int64_t)(tw_hi + 1) * L;
         for (int64_t rb = dlo; rb < dhi; rb += 32) {
-            // V rows of the block into the wave's slice (row-major); rows past the end are clamped.
-#pragma unroll
-            for (int i = 0; i < D / 16; ++i) {
-                const int c = lane + 64 * i, row = c / CH, ch = c % CH;
-                const int64_t r = min(rb + row, TL_rows - 1);
-                st16(vslice + row * KP + ch * 8, ld16(Vdb + r * D + ch * 8));
-            }
+            // V rows of the block into the wave's slice; rows past the end are clamped.
+            stage_rows<D>(vslice, 32, [&](int r) { return Vdb + min(rb + r, TL_rows - 1) * D; },
+                          lane, 0, 1);
             // K rows as A operands straight from HBM.
             f32x16 s[2];
             {
@@ -244,14 +223,11 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(FwdArgs a)
                 const int rj = (j >> 2) * 8 + (j & 3);
                 if (rj < lo || rj >= lo + L) s[0][j] = -INFINITY;
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             softmax_update<D, 1>(s, m, l, o, a.c);
-            pv_block<D, KP>(vslice, 0, s[0], o, lane);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            wait_vmem();
+            wave_lds_sync();
+            pv_block<D>(vslice, 0, s[0], o, lane);
+            wave_lds_sync();
         }
     }
 
