@@ -26,6 +26,8 @@
 //
 // Epilogue: O = o / sum in bf16 (round to nearest even) and
 // lse = scale*m + ln(sum) in fp32.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -69,7 +71,7 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[2], float& m, float& 
 #pragma unroll
         for (int j = 0; j < 16; ++j) mt = fmaxf(mt, s[kb][j]);
     mt = max_halves(mt);
-    const bool grow = (mt - m) * c > kRescaleLog2;   // true when m is still -inf
+    const bool grow = (mt - m) * c > kRescaleLog2;   // true for the first visible score
     if (__any(grow)) {
         const float m_new = fmaxf(m, mt);
         const float alpha = fast_exp2((m - m_new) * c);
@@ -100,7 +102,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(FwdArgs a)
     constexpr int ELEMS = BN * TL::PITCH;      // one K or V tile
     static_assert(BN % (TL::RPI * NW) == 0, "tile staging must divide evenly");
     constexpr int BM = NW * 32;
-    // [buf][K or V][BN rows]; the depth phase reuses it as NW private 32-row slices.
+    // [buf][K or V][BN rows]; after the sequence loop it holds NW private 32-row
+    // depth slices.  64 KiB: a CU can start its next workgroup while this one drains.
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * ELEMS];
     static_assert(NW * 32 * TL::PITCH <= 2 * 2 * ELEMS, "depth slices must fit");
 
@@ -144,30 +147,126 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(FwdArgs a)
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
-    float m = -INFINITY, l = 0.f;
+    // Running max: a finite sentinel, so that a block with no visible key for this lane
+    // gives weights exp2(-inf) = 0, never NaN; the first visible score always triggers a
+    // rescale (alpha = exp2(-huge) = 0).
+    float m = -1e30f, l = 0.f;
 
-    // ---- sequence phase ----
-    const int ntiles = t_hi_wg / BN + 1;
-    // K and V tile `tile` into buffer `buf` (direct global->LDS; rows past T repeat row T-1,
-    // whose weights are masked to zero).
-    auto stage = [&](int tile, int buf) {
-        uint16_t* ks = smem + (2 * buf) * ELEMS;
-        const int k0 = tile * BN;
-        stage_rows<D>(ks, BN, [&](int r) { return Kb + (int64_t)min(k0 + r, T - 1) * D; }, lane, w, NW);
-        stage_rows<D>(ks + ELEMS, BN, [&](int r) { return Vb + (int64_t)min(k0 + r, T - 1) * D; },
-                      lane, w, NW);
+    // ---- depth rows of this wave's tokens ----
+    // Rows [tw_lo*L, (tw_hi+1)*L) of the token-major depth KV, in blocks of 32.  A
+    // block's K rows are MFMA A operands loaded straight into registers, its V rows go
+    // to the wave's LDS slice (direct loads) for the transposed read.  Prefetch: the
+    // next block's K loads are issued as soon as the current scores have consumed the
+    // registers, its V loads as soon as the current PV has read the slice.  Mask: row r
+    // is visible to token t iff t*L <= r < t*L + L.
+    auto depth_phase = [&]() {
+        const int64_t TL_rows = (int64_t)T * L;
+        const uint16_t* Kdb = a.Kd + kvbase * (int64_t)L * D;
+        const uint16_t* Vdb = a.Vd + kvbase * (int64_t)L * D;
+        const int64_t dlo = (int64_t)tw_lo * L, dhi = (int64_t)(tw_hi + 1) * L;
+        const int nblk = (int)((dhi - dlo + 31) / 32);
+        uint16_t* slot = smem + w * 32 * D;
+        constexpr int NK = D / 16;                     // K loads per block (vector-memory instructions)
+        bf16x8 kr[D / 16];
+        auto issue_v = [&](int i) {
+            const int64_t rb = dlo + 32 * (int64_t)i;
+            if (rb + 32 <= TL_rows) {
+                const uint16_t* vt = Vdb + rb * D;
+                stage_rows<D>(slot, 32, [&](int r) { return vt + r * D; }, lane, 0, 1);
+            } else {
+                stage_rows<D>(slot, 32, [&](int r) { return Vdb + min(rb + r, TL_rows - 1) * D; },
+                              lane, 0, 1);
+            }
+        };
+        auto issue_k = [&](int i) {
+            const uint16_t* krow = Kdb + min(dlo + 32 * (int64_t)i + col, TL_rows - 1) * D + 8 * hf;
+#pragma unroll
+            for (int si = 0; si < D / 16; ++si) kr[si] = __builtin_bit_cast(bf16x8, ld16(krow + 16 * si));
+        };
+        if (nblk > 0) {
+            issue_v(0);
+            issue_k(0);
+        }
+        for (int i = 0; i < nblk; ++i) {
+            const bool more = i + 1 < nblk;
+            f32x16 s[2];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) s[0][j] = 0.f;
+#pragma unroll
+            for (int si = 0; si < D / 16; ++si) s[0] = mfma32(kr[si], qreg[si], s[0]);
+            if (more) issue_k(i + 1);
+            const int64_t lo = (int64_t)tcol * L - dlo - 32 * (int64_t)i - 4 * hf;   // first visible row
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int rj = (j >> 2) * 8 + (j & 3);
+                if (rj < lo || rj >= lo + L) s[0][j] = -INFINITY;
+            }
+            softmax_update<D, 1>(s, m, l, o, a.c);
+            if (more) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NK) : "memory");   // V of block i landed
+            else wait_vmem();
+            wave_lds_sync();
+            pv_block<D>(slot, 0, s[0], o, lane);
+            wave_lds_sync();
+            if (more) issue_v(i + 1);
+        }
     };
 
-    stage(0, 0);
-    wait_vmem();
-    __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-        const int buf = it & 1;
-        if (it + 1 < ntiles) stage(it + 1, buf ^ 1);
+    // ---- sequence phase ----
+    // Per-lane LDS element offsets, fixed for the whole loop (the tile base and
+    // the 16-row-aligned block offsets below are compile-time immediates):
+    //   kofs[si]     K operand of S^T = K Q^T, row col, chunk of d = 16*si + 8*hf;
+    //   vofs[q][db]  transposed V read of pv_block, rows 8*q + 4*hf + (col%16)/4.
+    int kofs[D / 16], vofs[2][D / 32];
+#pragma unroll
+    for (int si = 0; si < D / 16; ++si) kofs[si] = TL::off(col, 16 * si + 8 * hf);
+    {
+        const int krow = 4 * hf + ((col & 15) >> 2), dcol = 16 * (col >> 4) + 4 * (col & 3);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) vofs[q][db] = TL::off(krow + 8 * q, dcol + 32 * db);
+    }
+    // Direct-load staging: instruction i of this wave fills rows (w + i*NW)*RPI .. +RPI of a
+    // tile; sofs[i] is this lane's element offset inside the global tile.
+    constexpr int NI = BN / (TL::RPI * NW);
+    int sofs[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int r = (w + i * NW) * TL::RPI + lane / TL::CPR;
+        sofs[i] = r * D + ((lane % TL::CPR) ^ TL::swz(r)) * 8;
+    }
+    const int ntiles = t_hi_wg / BN + 1;
+    const int t_lo_wg = (int)min(r0 / G, (int64_t)T - 1);
+    const int n_full = (t_lo_wg + 1) / BN;     // tiles no wave of this workgroup needs to mask
+
+    auto stage = [&](int tile, uint16_t* ks) {
+        const int k0 = tile * BN;
+        if (k0 + BN <= T) {
+            const uint16_t* kt = Kb + (int64_t)k0 * D;
+            const uint16_t* vt = Vb + (int64_t)k0 * D;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                uint16_t* dst = ks + (w + i * NW) * TL::RPI * D;
+                __builtin_amdgcn_global_load_lds((glob_void_t*)(kt + sofs[i]), (lds_void_t*)dst, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((glob_void_t*)(vt + sofs[i]), (lds_void_t*)(dst + ELEMS),
+                                                 16, 0, 0);
+            }
+        } else {   // the sequence's last tile: rows past T repeat row T-1 (their weights are 0)
+            stage_rows<D>(ks, BN, [&](int r) { return Kb + (int64_t)min(k0 + r, T - 1) * D; }, lane, w, NW);
+            stage_rows<D>(ks + ELEMS, BN, [&](int r) { return Vb + (int64_t)min(k0 + r, T - 1) * D; },
+                          lane, w, NW);
+        }
+    };
+
+    // One key tile from buffer BUF (0/1); MASKED tiles may reach past some wave's first token.
+    auto step = [&](auto bufc, auto maskc, int it) {
+        constexpr int BUF = decltype(bufc)::value;
+        constexpr bool MASKED = decltype(maskc)::value;
+        const uint16_t* ks = smem + 2 * BUF * ELEMS;
+        const uint16_t* vs = ks + ELEMS;
+        if (it + 1 < ntiles) stage(it + 1, smem + 2 * (BUF ^ 1) * ELEMS);
         const int k0 = it * BN;
-        if (k0 <= tw_hi) {
-            const uint16_t* ks = smem + (2 * buf) * ELEMS;
-            const uint16_t* vs = ks + ELEMS;
+        if (!MASKED || k0 <= tw_hi) {
             f32x16 s[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -175,9 +274,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(FwdArgs a)
                 for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
 #pragma unroll
                 for (int si = 0; si < D / 16; ++si)
-                    s[kb] = mfma32(lds_chunk<D>(ks, kb * 32 + col, 16 * si + 8 * hf), qreg[si], s[kb]);
+                    s[kb] = mfma32(*(const bf16x8*)(ks + kofs[si] + kb * 32 * D), qreg[si], s[kb]);
             }
-            if (k0 + BN - 1 > tw_lo) {   // tile reaches past the wave's first token: causal mask
+            if (MASKED && k0 + BN - 1 > tw_lo) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -187,49 +286,50 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(FwdArgs a)
                     }
             }
             softmax_update<D, 2>(s, m, l, o, a.c);
-            pv_block<D>(vs, 0, s[0], o, lane);
-            pv_block<D>(vs, 32, s[1], o, lane);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int sp = 0; sp < 2; ++sp) {
+                    const f32x16& p = s[kb];
+                    const bf16x8 pb = to_bf16x8(p[8 * sp + 0], p[8 * sp + 1], p[8 * sp + 2],
+                                                p[8 * sp + 3], p[8 * sp + 4], p[8 * sp + 5],
+                                                p[8 * sp + 6], p[8 * sp + 7]);
+                    const int rowoff = (kb * 32 + 16 * sp) * D;
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) {
+                        const bf16x4 lo = lds_read_tr(vs + vofs[0][db] + rowoff);
+                        const bf16x4 hi = lds_read_tr(vs + vofs[1][db] + rowoff);
+                        const bf16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        o[db] = mfma32(av, pb, o[db]);
+                    }
+                }
         }
         wait_vmem();
         __syncthreads();
-    }
+    };
 
-    // ---- depth phase: this wave's tokens only ----
-    if (L > 0) {
-        uint16_t* vslice = smem + w * 32 * TL::PITCH;   // private 32-row slice of the idle tiles
-        const int64_t TL_rows = (int64_t)T * L;
-        const uint16_t* Kdb = a.Kd + kvbase * (int64_t)L * D;
-        const uint16_t* Vdb = a.Vd + kvbase * (int64_t)L * D;
-        const int64_t dlo = (int64_t)tw_lo * L, dhi = (int64_t)(tw_hi + 1) * L;
-        for (int64_t rb = dlo; rb < dhi; rb += 32) {
-            // V rows of the block into the wave's slice; rows past the end are clamped.
-            stage_rows<D>(vslice, 32, [&](int r) { return Vdb + min(rb + r, TL_rows - 1) * D; },
-                          lane, 0, 1);
-            // K rows as A operands straight from HBM.
-            f32x16 s[2];
-            {
-                const int64_t r = min(rb + col, TL_rows - 1);
-                const uint16_t* krow = Kdb + r * D + 8 * hf;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) s[0][j] = 0.f;
-#pragma unroll
-                for (int si = 0; si < D / 16; ++si)
-                    s[0] = mfma32(__builtin_bit_cast(bf16x8, ld16(krow + 16 * si)), qreg[si], s[0]);
-            }
-            // Row rb + (j/4)*8 + 4*hf + j%4 is visible iff it lies in [tcol*L, tcol*L + L).
-            const int64_t lo = (int64_t)tcol * L - rb - 4 * hf;   // first visible row index
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int rj = (j >> 2) * 8 + (j & 3);
-                if (rj < lo || rj >= lo + L) s[0][j] = -INFINITY;
-            }
-            softmax_update<D, 1>(s, m, l, o, a.c);
-            wait_vmem();
-            wave_lds_sync();
-            pv_block<D>(vslice, 0, s[0], o, lane);
-            wave_lds_sync();
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using BF = std::integral_constant<bool, false>;
+    using BT = std::integral_constant<bool, true>;
+    stage(0, smem);
+    wait_vmem();
+    __syncthreads();
+    int it = 0;
+    for (; it + 1 < n_full; it += 2) {
+        step(I0(), BF(), it);
+        step(I1(), BF(), it + 1);
+    }
+    for (; it < ntiles; ++it) {
+        if (it < n_full) {
+            if (it & 1) step(I1(), BF(), it);
+            else step(I0(), BF(), it);
+        } else {
+            if (it & 1) step(I1(), BT(), it);
+            else step(I0(), BT(), it);
         }
     }
+    if (L > 0) depth_phase();
 
     // ---- epilogue ----
     if (valid) {
