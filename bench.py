@@ -142,6 +142,28 @@ def traffic_for(label):
     return None
 
 
+def fwd_overhead(step, step0, rounds=8):
+    """Depth overhead of the forward measured with interleaved launches: each round
+    times moda_fwd with depth (L) and without (L=0) back to back, so clock drift
+    affects both alike.  Returns median milliseconds of each."""
+    torch, mb = step.torch, step.mb
+    x, x0 = step.x, step0.x
+    tl, t0 = [], []
+    for _ in range(rounds):
+        for st, xx, acc in ((step, x, tl), (step0, x0, t0)):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(2):
+                mb.moda_fwd(st.p, xx["Q"], xx["K"], xx["V"], st.Kd, st.Vd, st.O, st.lse)
+            e1.record()
+            torch.cuda.synchronize()
+            acc.append(e0.elapsed_time(e1) / 2)
+    tl.sort()
+    t0.sort()
+    return tl[len(tl) // 2], t0[len(t0) // 2]
+
+
 def kernel_work(label, w):
     """Algorithmic work of one launch of a libmoda kernel: (bound, amount, unit).
 
@@ -248,7 +270,8 @@ def main():
         torch.cuda.empty_cache()
         s0 = Step(w, 0, seed=0)
         ms0, k0, _ = s0.timed(args.steps, args.warmup)
-        res0 = {"ms_per_step": ms0, "kernels": k0}
+        fl, f0 = fwd_overhead(step, s0)
+        res0 = {"ms_per_step": ms0, "kernels": k0, "fwd_interleaved": (fl, f0)}
         del s0
         torch.cuda.empty_cache()
 
@@ -302,7 +325,10 @@ def main():
         out["l0"] = {"ms_per_step": round(res0["ms_per_step"], 3), "fwd_ms": round(fwd_0, 3),
                      "bwd_ms": round(bwd_0, 3),
                      "fwd_tflops": round(fwd_flops(w, 0) / (fwd_0 * 1e-3) / 1e12, 2)}
+        fl, f0 = res0["fwd_interleaved"]
+        out["l0"]["fwd_interleaved_ms"] = {"L": round(fl, 3), "L0": round(f0, 3)}
         out["overhead"] = {
+            "fwd_interleaved": round((fl - f0) / f0, 4),
             "fwd": round((fwd_l - fwd_0) / fwd_0, 4),
             "fwd_bwd": round((fwd_l + bwd_l - fwd_0 - bwd_0) / (fwd_0 + bwd_0), 4),
             "step": round((ms - res0["ms_per_step"]) / res0["ms_per_step"], 4),

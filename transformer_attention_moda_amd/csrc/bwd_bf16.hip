@@ -22,6 +22,8 @@
 //   bwd_depth  per wave, its tokens' depth rows: S_d = Q Kd^T (lane = depth
 //              row), dVd^T += dO^T P_d, dKd^T += Q^T dS_d.  A token's G heads sit
 //              in one wave, so every depth row is finished by one wave.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -226,11 +228,11 @@ template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
 {
     using TL = LdsTile<D>;
-    constexpr int KP = TL::PITCH;
     static_assert(BQ % (TL::RPI * NW) == 0, "tile staging must divide evenly");
     constexpr int BK = NW * 32;   // keys per workgroup
+    constexpr int TILE = BQ * D;  // elements of one Q or dO tile
     // [buf][Q, dO][BQ rows] then [buf][lse2, D][BQ]
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * BQ * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
     __shared__ __attribute__((aligned(16))) float srow[2][2][BQ];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -258,88 +260,132 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
     f32x16 dk[D / 32], dv[D / 32];
     zero(dk);
     zero(dv);
+    LaneOffsets<D> lo;
+    lo.init(lane);
 
     const int64_t TG = (int64_t)T * G;
-    const int64_t f_start = (int64_t)min(k0, T) * G;   // first folded row that sees a key of this block
+    const int64_t f_start = (int64_t)k0 * G;   // first folded row that sees a key of this block
     const int ntiles = (int)((TG - f_start + BQ - 1) / BQ);
+    const int n_mask = min(ntiles, ((BK - 1) * G + BQ - 1) / BQ);   // tiles reaching below key k0+BK-1
     const int64_t qhead0 = (int64_t)b * a.Hq + (int64_t)kv * G;
 
-    // Query tile `tile` (folded rows f0 .. f0+BQ-1) into buffer `buf`: Q and dO rows by direct
-    // loads (rows past the end repeat the last row; their lse is +inf so their weights are 0),
-    // lse2 and D through registers by the first BQ threads.
+    // Folded row f0 + r (f0 a multiple of BQ, G | BQ) is query head qhead0 + r%G at token
+    // f0/G + r/G: a uniform base plus a per-lane constant.
+    constexpr int NI = BQ / (TL::RPI * NW);
+    int sofs[NI];
+#pragma unroll
+    for (int i2 = 0; i2 < NI; ++i2) {
+        const int r = (w + i2 * NW) * TL::RPI + lane / TL::CPR;
+        sofs[i2] = (int)(((int64_t)(r & (G - 1)) * T + (r >> lgG)) * D) +
+                   ((lane % TL::CPR) ^ TL::swz(r)) * 8;
+    }
+    const int64_t rofs = (int64_t)(tid & (G - 1)) * T + (tid >> lgG);   // lse/D row offset (tid < BQ)
     float lst = 0.f, dvst = 0.f;
     auto qi_of = [&](int64_t f) {
         f = min(f, TG - 1);
         return (qhead0 + (f & (G - 1))) * T + (f >> lgG);
     };
-    auto stage = [&](int tile, int buf) {
+    auto stage = [&](int tile, uint16_t* qs) {
         const int64_t f0 = f_start + (int64_t)tile * BQ;
-        uint16_t* qs = smem + (2 * buf) * BQ * KP;
-        stage_rows<D>(qs, BQ, [&](int r) { return a.Q + qi_of(f0 + r) * D; }, lane, w, NW);
-        stage_rows<D>(qs + BQ * KP, BQ, [&](int r) { return a.dO + qi_of(f0 + r) * D; }, lane, w,
-                      NW);
-        if (tid < BQ) {
-            const int64_t f = f0 + tid;
-            lst = f < TG ? a.lse2[qi_of(f)] : INFINITY;
-            dvst = f < TG ? a.Dv[qi_of(f)] : 0.f;
-        }
-    };
-    auto sstore_rows = [&](int buf) {
-        if (tid < BQ) {
-            srow[buf][0][tid] = lst;
-            srow[buf][1][tid] = dvst;
+        if (f0 + BQ <= TG) {
+            const int64_t base = qhead0 * T + (f0 >> lgG);
+            const uint16_t* qt = a.Q + base * D;
+            const uint16_t* dt = a.dO + base * D;
+#pragma unroll
+            for (int i2 = 0; i2 < NI; ++i2) {
+                uint16_t* dst = qs + (w + i2 * NW) * TL::RPI * D;
+                __builtin_amdgcn_global_load_lds((glob_void_t*)(qt + sofs[i2]), (lds_void_t*)dst, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((glob_void_t*)(dt + sofs[i2]), (lds_void_t*)(dst + TILE),
+                                                 16, 0, 0);
+            }
+            if (tid < BQ) {
+                lst = a.lse2[base + rofs];
+                dvst = a.Dv[base + rofs];
+            }
+        } else {   // the last tile: rows past the end repeat the last row with lse +inf (weight 0)
+            stage_rows<D>(qs, BQ, [&](int r) { return a.Q + qi_of(f0 + r) * D; }, lane, w, NW);
+            stage_rows<D>(qs + TILE, BQ, [&](int r) { return a.dO + qi_of(f0 + r) * D; }, lane, w, NW);
+            if (tid < BQ) {
+                const int64_t f = f0 + tid;
+                lst = f < TG ? a.lse2[qi_of(f)] : INFINITY;
+                dvst = f < TG ? a.Dv[qi_of(f)] : 0.f;
+            }
         }
     };
 
     const float c = a.c;
-    if (ntiles > 0) {
-        stage(0, 0);
-        sstore_rows(0);
-    }
-    wait_vmem();
-    __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-        const int buf = it & 1;
-        if (it + 1 < ntiles) stage(it + 1, buf ^ 1);
-        const uint16_t* qs = smem + (2 * buf) * BQ * KP;
-        const uint16_t* ds = qs + BQ * KP;
+    auto step = [&](auto bufc, auto maskc, int it) {
+        constexpr int BUF = decltype(bufc)::value;
+        constexpr bool MASKED = decltype(maskc)::value;
+        const uint16_t* qs = smem + 2 * BUF * TILE;
+        const uint16_t* ds = qs + TILE;
+        if (it + 1 < ntiles) stage(it + 1, smem + 2 * (BUF ^ 1) * TILE);
         const int64_t f0 = f_start + (int64_t)it * BQ;
 #pragma unroll
         for (int qb = 0; qb < BQ / 32; ++qb) {
             const int64_t fb = f0 + qb * 32;
-            const int64_t tb_hi = (fb + 31) >> lgG;       // last token of the block
-            if (tb_hi < kw || fb >= TG) continue;         // wave-uniform: nothing visible
-            f32x16 s, dp;
+            if (MASKED && (((fb + 31) >> lgG) < kw || fb >= TG)) continue;   // nothing visible
+            f32x16 sv, dp;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) s[j] = dp[j] = 0.f;
+            for (int j = 0; j < 16; ++j) sv[j] = dp[j] = 0.f;
 #pragma unroll
             for (int si = 0; si < D / 16; ++si) {
-                s = mfma32(lds_chunk<D>(qs, qb * 32 + col, 16 * si + 8 * hf), kreg[si], s);
-                dp = mfma32(lds_chunk<D>(ds, qb * 32 + col, 16 * si + 8 * hf), vreg[si], dp);
+                sv = mfma32(*(const bf16x8*)(qs + lo.a[si] + qb * 32 * D), kreg[si], sv);
+                dp = mfma32(*(const bf16x8*)(ds + lo.a[si] + qb * 32 * D), vreg[si], dp);
             }
-            const bool need_mask = (fb >> lgG) < kw + 31;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int rbase = qb * 32 + jj * 8 + 4 * hf;
-                const float4 l4 = *(const float4*)&srow[buf][0][rbase];
-                const float4 d4 = *(const float4*)&srow[buf][1][rbase];
+                const float4 l4 = *(const float4*)&srow[BUF][0][rbase];
+                const float4 d4 = *(const float4*)&srow[BUF][1][rbase];
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int j = 4 * jj + e;
-                    float p = fast_exp2(fmaf(s[j], c, -lv[e]));
-                    if (need_mask && ((fb + jj * 8 + 4 * hf + e) >> lgG) < key) p = 0.f;
-                    s[j] = p;
-                    dp[j] = p * (dp[j] - dvv[e]);
+                    float pr = fast_exp2(fmaf(sv[j], c, -lv[e]));
+                    if (MASKED && ((fb + jj * 8 + 4 * hf + e) >> lgG) < key) pr = 0.f;
+                    sv[j] = pr;
+                    dp[j] = pr * (dp[j] - dvv[e]);
                 }
             }
-            pv_block<D>(ds, qb * 32, s, dv, lane);
-            pv_block<D>(qs, qb * 32, dp, dk, lane);
+            pv_block_pre<D>(ds + qb * 32 * D, sv, dv, lo);
+            pv_block_pre<D>(qs + qb * 32 * D, dp, dk, lo);
         }
-        if (it + 1 < ntiles) sstore_rows(buf ^ 1);
+        if (it + 1 < ntiles && tid < BQ) {
+            srow[BUF ^ 1][0][tid] = lst;
+            srow[BUF ^ 1][1][tid] = dvst;
+        }
         wait_vmem();
         __syncthreads();
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using BF = std::integral_constant<bool, false>;
+    using BT = std::integral_constant<bool, true>;
+    if (ntiles > 0) {
+        stage(0, smem);
+        if (tid < BQ) {
+            srow[0][0][tid] = lst;
+            srow[0][1][tid] = dvst;
+        }
     }
+    wait_vmem();
+    __syncthreads();
+    int it = 0;
+    for (; it < n_mask; ++it) {
+        if (it & 1) step(I1(), BT(), it);
+        else step(I0(), BT(), it);
+    }
+    if (it < ntiles && (it & 1)) {
+        step(I1(), BF(), it);
+        ++it;
+    }
+    for (; it + 1 < ntiles; it += 2) {
+        step(I0(), BF(), it);
+        step(I1(), BF(), it + 1);
+    }
+    if (it < ntiles) step(I0(), BF(), it);
     if (kvalid) {
         store_row_bf16<D>(a.dK + (kvbase + key) * D, dk, a.scale, lane);
         store_row_bf16<D>(a.dV + (kvbase + key) * D, dv, 1.f, lane);

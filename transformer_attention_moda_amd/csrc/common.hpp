@@ -140,6 +140,51 @@ __device__ __forceinline__ void pv_block(const uint16_t* x, int row0, const f32x
     }
 }
 
+// Per-lane LDS element offsets inside an LdsTile<D>, computed once per kernel:
+//   a[si]     the 16-byte MFMA operand chunk of row l%32, elements 16*si + 8*(l/32) .. +8
+//             (A operand of K/Q/dO rows, or B operand of the same layout);
+//   t[q][db]  the transposed read of pv_block: rows 8*q + 4*(l/32) + (l%16)/4,
+//             elements 16*((l%32)/16) + 4*(l%4) + 32*db.
+// Adding a multiple of 16 rows (16*D elements) keeps both valid, because the
+// swizzle depends on the row modulo 16, so loops address tiles with per-lane
+// registers plus compile-time immediates.
+template <int D>
+struct LaneOffsets {
+    int a[D / 16];
+    int t[2][D / 32];
+    __device__ __forceinline__ void init(int lane)
+    {
+        const int col = lane & 31, hf = lane >> 5;
+#pragma unroll
+        for (int si = 0; si < D / 16; ++si) a[si] = LdsTile<D>::off(col, 16 * si + 8 * hf);
+        const int krow = 4 * hf + ((col & 15) >> 2), dcol = 16 * (col >> 4) + 4 * (col & 3);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) t[q][db] = LdsTile<D>::off(krow + 8 * q, dcol + 32 * db);
+    }
+};
+
+// pv_block with precomputed offsets: tile points at row 0 of the 32-row block
+// (a multiple of 16 rows into an LdsTile<D>).
+template <int D>
+__device__ __forceinline__ void pv_block_pre(const uint16_t* tile, const f32x16& p,
+                                             f32x16 (&acc)[D / 32], const LaneOffsets<D>& lo)
+{
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+        const bf16x8 pb = to_bf16x8(p[8 * sp + 0], p[8 * sp + 1], p[8 * sp + 2], p[8 * sp + 3],
+                                    p[8 * sp + 4], p[8 * sp + 5], p[8 * sp + 6], p[8 * sp + 7]);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const bf16x4 x0 = lds_read_tr(tile + lo.t[0][db] + 16 * sp * D);
+            const bf16x4 x1 = lds_read_tr(tile + lo.t[1][db] + 16 * sp * D);
+            const bf16x8 av = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+            acc[db] = mfma32(av, pb, acc[db]);
+        }
+    }
+}
+
 // The 16-byte MFMA operand chunk (elements 8*c .. 8*c+7) of row `row`.
 template <int D>
 __device__ __forceinline__ bf16x8 lds_chunk(const uint16_t* tile, int row, int elem)
