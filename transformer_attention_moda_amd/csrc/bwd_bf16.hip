@@ -134,51 +134,94 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
     f32x16 dq[D / 32];
     zero(dq);
 
+    LaneOffsets<D> lo;
+    lo.init(lane);
+    constexpr int NI = BN / (TL::RPI * NW);
+    int sofs[NI];
+#pragma unroll
+    for (int i2 = 0; i2 < NI; ++i2) {
+        const int r = (w + i2 * NW) * TL::RPI + lane / TL::CPR;
+        sofs[i2] = r * D + ((lane % TL::CPR) ^ TL::swz(r)) * 8;
+    }
     const int ntiles = t_hi_wg / BN + 1;
-    auto stage = [&](int tile, int buf) {
-        uint16_t* ks = smem + (2 * buf) * ELEMS;
+    const int t_lo_wg = (int)min(r0 / G, (int64_t)T - 1);
+    const int n_full = (t_lo_wg + 1) / BN;     // tiles no wave of this workgroup needs to mask
+    auto stage = [&](int tile, uint16_t* ks) {
         const int k0 = tile * BN;
-        stage_rows<D>(ks, BN, [&](int r) { return Kb + (int64_t)min(k0 + r, T - 1) * D; }, lane, w, NW);
-        stage_rows<D>(ks + ELEMS, BN, [&](int r) { return Vb + (int64_t)min(k0 + r, T - 1) * D; },
-                      lane, w, NW);
+        if (k0 + BN <= T) {
+            const uint16_t* kt = Kb + (int64_t)k0 * D;
+            const uint16_t* vt = Vb + (int64_t)k0 * D;
+#pragma unroll
+            for (int i2 = 0; i2 < NI; ++i2) {
+                uint16_t* dst = ks + (w + i2 * NW) * TL::RPI * D;
+                __builtin_amdgcn_global_load_lds((glob_void_t*)(kt + sofs[i2]), (lds_void_t*)dst, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((glob_void_t*)(vt + sofs[i2]), (lds_void_t*)(dst + ELEMS),
+                                                 16, 0, 0);
+            }
+        } else {   // the sequence's last tile: rows past T repeat row T-1 (their weights are 0)
+            stage_rows<D>(ks, BN, [&](int r) { return Kb + (int64_t)min(k0 + r, T - 1) * D; }, lane, w, NW);
+            stage_rows<D>(ks + ELEMS, BN, [&](int r) { return Vb + (int64_t)min(k0 + r, T - 1) * D; },
+                          lane, w, NW);
+        }
     };
-
-    stage(0, 0);
-    wait_vmem();
-    __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-        const int buf = it & 1;
-        if (it + 1 < ntiles) stage(it + 1, buf ^ 1);
+    auto step = [&](auto bufc, auto maskc, int it) {
+        constexpr int BUF = decltype(bufc)::value;
+        constexpr bool MASKED = decltype(maskc)::value;
+        const uint16_t* ks = smem + 2 * BUF * ELEMS;
+        const uint16_t* vs = ks + ELEMS;
+        if (it + 1 < ntiles) stage(it + 1, smem + 2 * (BUF ^ 1) * ELEMS);
         const int k0 = it * BN;
-        if (k0 <= tw_hi) {
-            const uint16_t* ks = smem + (2 * buf) * ELEMS;
-            const uint16_t* vs = ks + ELEMS;
-            f32x16 s[2], dp[2];
+        if (!MASKED || k0 <= tw_hi) {
+            f32x16 sv[2], dp[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-                for (int j = 0; j < 16; ++j) s[kb][j] = dp[kb][j] = 0.f;
+                for (int j = 0; j < 16; ++j) sv[kb][j] = dp[kb][j] = 0.f;
 #pragma unroll
                 for (int si = 0; si < D / 16; ++si) {
-                    s[kb] = mfma32(lds_chunk<D>(ks, kb * 32 + col, 16 * si + 8 * hf), qreg[si], s[kb]);
-                    dp[kb] = mfma32(lds_chunk<D>(vs, kb * 32 + col, 16 * si + 8 * hf), dreg[si], dp[kb]);
+                    sv[kb] = mfma32(*(const bf16x8*)(ks + lo.a[si] + kb * 32 * D), qreg[si], sv[kb]);
+                    dp[kb] = mfma32(*(const bf16x8*)(vs + lo.a[si] + kb * 32 * D), dreg[si], dp[kb]);
                 }
             }
-            const bool need_mask = k0 + BN - 1 > tw_lo;
+            const bool need_mask = MASKED && k0 + BN - 1 > tw_lo;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const int key = k0 + kb * 32 + (j >> 2) * 8 + hf * 4 + (j & 3);
-                    float p = fast_exp2(fmaf(s[kb][j], c, -lse2));
-                    if (need_mask && key > tcol) p = 0.f;
-                    s[kb][j] = p * (dp[kb][j] - Dr);
+                    float pr = fast_exp2(fmaf(sv[kb][j], c, -lse2));
+                    if (MASKED) {
+                        const int key = k0 + kb * 32 + (j >> 2) * 8 + hf * 4 + (j & 3);
+                        if (need_mask && key > tcol) pr = 0.f;
+                    }
+                    sv[kb][j] = pr * (dp[kb][j] - Dr);
                 }
-            pv_block<D>(ks, 0, s[0], dq, lane);
-            pv_block<D>(ks, 32, s[1], dq, lane);
+            pv_block_pre<D>(ks, sv[0], dq, lo);
+            pv_block_pre<D>(ks + 32 * D, sv[1], dq, lo);
         }
         wait_vmem();
         __syncthreads();
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using BF = std::integral_constant<bool, false>;
+    using BT = std::integral_constant<bool, true>;
+    stage(0, smem);
+    wait_vmem();
+    __syncthreads();
+    int it = 0;
+    for (; it + 1 < n_full; it += 2) {
+        step(I0(), BF(), it);
+        step(I1(), BF(), it + 1);
+    }
+    for (; it < ntiles; ++it) {
+        if (it < n_full) {
+            if (it & 1) step(I1(), BF(), it);
+            else step(I0(), BF(), it);
+        } else {
+            if (it & 1) step(I1(), BT(), it);
+            else step(I0(), BT(), it);
+        }
     }
 
     // Depth rows of this wave's tokens: dQ^T += Kd^T dS_d^T.
