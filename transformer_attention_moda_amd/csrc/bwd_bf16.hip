@@ -364,18 +364,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
         const uint16_t* ds = qs + TILE;
         if (it + 1 < ntiles) stage(it + 1, smem + 2 * (BUF ^ 1) * TILE);
         const int64_t f0 = f_start + (int64_t)it * BQ;
-#pragma unroll
-        for (int qb = 0; qb < BQ / 32; ++qb) {
+        // Weights of block qb: P = exp2(S c - lse2) (masked), dS = P (dP - D).
+        auto weights = [&](int qb, f32x16& sv, f32x16& dp) {
             const int64_t fb = f0 + qb * 32;
-            if (MASKED && (((fb + 31) >> lgG) < kw || fb >= TG)) continue;   // nothing visible
-            f32x16 sv, dp;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) sv[j] = dp[j] = 0.f;
-#pragma unroll
-            for (int si = 0; si < D / 16; ++si) {
-                sv = mfma32(*(const bf16x8*)(qs + lo.a[si] + qb * 32 * D), kreg[si], sv);
-                dp = mfma32(*(const bf16x8*)(ds + lo.a[si] + qb * 32 * D), vreg[si], dp);
-            }
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int rbase = qb * 32 + jj * 8 + 4 * hf;
@@ -391,8 +382,75 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
                     dp[j] = pr * (dp[j] - dvv[e]);
                 }
             }
-            pv_block_pre<D>(ds + qb * 32 * D, sv, dv, lo);
-            pv_block_pre<D>(qs + qb * 32 * D, dp, dk, lo);
+        };
+        if (MASKED) {
+#pragma unroll
+            for (int qb = 0; qb < BQ / 32; ++qb) {
+                const int64_t fb = f0 + qb * 32;
+                if (((fb + 31) >> lgG) < kw || fb >= TG) continue;   // nothing visible
+                f32x16 sv, dp;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) sv[j] = dp[j] = 0.f;
+#pragma unroll
+                for (int si = 0; si < D / 16; ++si) {
+                    sv = mfma32(*(const bf16x8*)(qs + lo.a[si] + qb * 32 * D), kreg[si], sv);
+                    dp = mfma32(*(const bf16x8*)(ds + lo.a[si] + qb * 32 * D), vreg[si], dp);
+                }
+                weights(qb, sv, dp);
+                pv_block_pre<D>(ds + qb * 32 * D, sv, dv, lo);
+                pv_block_pre<D>(qs + qb * 32 * D, dp, dk, lo);
+            }
+        } else {
+            // Both blocks' scores first, so that block 0's weights overlap block 1's
+            // products and block 1's weights overlap block 0's gradient products.
+            f32x16 sv[2], dp[2];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) sv[qb][j] = dp[qb][j] = 0.f;
+#pragma unroll
+                for (int si = 0; si < D / 16; ++si) {
+                    sv[qb] = mfma32(*(const bf16x8*)(qs + lo.a[si] + qb * 32 * D), kreg[si], sv[qb]);
+                    dp[qb] = mfma32(*(const bf16x8*)(ds + lo.a[si] + qb * 32 * D), vreg[si], dp[qb]);
+                }
+            }
+            weights(0, sv[0], dp[0]);
+            pv_block_pre<D>(ds, sv[0], dv, lo);
+            pv_block_pre<D>(qs, dp[0], dk, lo);
+            weights(1, sv[1], dp[1]);
+            pv_block_pre<D>(ds + 32 * D, sv[1], dv, lo);
+            pv_block_pre<D>(qs + 32 * D, dp[1], dk, lo);
+            // Issue order (one wave per SIMD, so nothing else hides LDS latency): LA
+            // operand reads ahead of the score MFMAs, GA read pairs of the gradient
+            // products issued during the last score MFMAs, and each block's weight
+            // arithmetic spread over MFMAs that do not depend on it.
+            constexpr int NM = D / 8;   // score MFMAs per block (S and dP)
+            constexpr int NG = D / 8;   // gradient MFMAs per block (dV and dK)
+            constexpr int LA = 8, GA = 8;
+            SCHED_GROUP(kSchedDsRead, LA);
+#pragma unroll
+            for (int i = 0; i < 2 * NM - LA; ++i) {
+                SCHED_GROUP(kSchedMfma, 1);
+                SCHED_GROUP(kSchedDsRead, 1);
+                if (i >= NM) SCHED_GROUP(kSchedValu, 5);
+            }
+#pragma unroll
+            for (int i = 0; i < LA; ++i) {
+                SCHED_GROUP(kSchedMfma, 1);
+                SCHED_GROUP(kSchedDsRead, 2 * GA / LA);
+                SCHED_GROUP(kSchedValu, 5);
+            }
+#pragma unroll
+            for (int i = 0; i < NG; ++i) {
+                SCHED_GROUP(kSchedMfma, 1);
+                SCHED_GROUP(kSchedDsRead, 2);
+                SCHED_GROUP(kSchedValu, 5);
+            }
+#pragma unroll
+            for (int i = 0; i < NG; ++i) {
+                SCHED_GROUP(kSchedMfma, 1);
+                SCHED_GROUP(kSchedDsRead, 2);
+            }
         }
         if (it + 1 < ntiles && tid < BQ) {
             srow[BUF ^ 1][0][tid] = lst;

@@ -110,6 +110,14 @@ __device__ __forceinline__ void stage_rows(uint16_t* tile, int nrows, RowPtr row
     }
 }
 
+// Instruction classes for SCHED_GROUP: the compiler's scheduler places the
+// next `count` instructions of the class at this point of the issue order
+// (among those of the enclosing basic block), in program order of the calls.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedValu = 0x002 | 0x400;   // vector ALU including transcendentals
+#define SCHED_GROUP(mask, count) __builtin_amdgcn_sched_group_barrier((mask), (count), 0)
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // acc^T += X^T P for a block of 32 rows of X held in LDS rows [row0, row0+32)
