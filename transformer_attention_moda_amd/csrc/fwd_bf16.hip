@@ -95,15 +95,17 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[2], float& m, float& 
     l += sum_halves(ps);
 }
 
+// Eight waves per CU either way: one 8-wave workgroup (256 rows) or two 4-wave
+// workgroups (128 rows), two waves per SIMD and at most 256 registers per wave.
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_kernel(FwdArgs a)
+__global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
 {
     using TL = LdsTile<D>;
     constexpr int ELEMS = BN * TL::PITCH;      // one K or V tile
     static_assert(BN % (TL::RPI * NW) == 0, "tile staging must divide evenly");
     constexpr int BM = NW * 32;
     // [buf][K or V][BN rows]; after the sequence loop it holds NW private 32-row
-    // depth slices.  64 KiB: a CU can start its next workgroup while this one drains.
+    // depth slices.
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * ELEMS];
     static_assert(NW * 32 * TL::PITCH <= 2 * 2 * ELEMS, "depth slices must fit");
 
