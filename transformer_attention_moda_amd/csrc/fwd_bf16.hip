@@ -61,7 +61,7 @@ constexpr float kRescaleLog2 = 8.f;
 // wave would otherwise see a weight above 2^kRescaleLog2; o/l = softmax output
 // holds for any m, so keeping a stale m is exact.  On return s holds the
 // weights exp2(c*(score - m)).
-template <int D, int NB>
+template <int D, int NB, bool SUM = true>
 __device__ __forceinline__ void softmax_update(f32x16 (&s)[2], float& m, float& l,
                                                f32x16 (&o)[D / 32], float c)
 {
@@ -92,7 +92,18 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[2], float& m, float& 
             s[kb][j] = p;
             ps += p;
         }
-    l += sum_halves(ps);
+    if (SUM) l += sum_halves(ps);
+}
+
+// Adds the 8 bf16 values of p to acc (packed dot products with 1): the row sum of
+// exactly the weights the PV product consumes, at half the instructions of fp32 adds.
+__device__ __forceinline__ float row_sum_bf16(const bf16x8& p, float acc)
+{
+    const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[2 * i], p[2 * i + 1]}, one, acc, false);
+    return acc;
 }
 
 // Eight waves per CU either way: one 8-wave workgroup (256 rows) or two 4-wave
@@ -271,13 +282,22 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
         if (!MASKED || k0 <= tw_hi) {
             f32x16 s[2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int j = 0; j < 16; ++j) s[0][j] = s[1][j] = 0.f;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
-#pragma unroll
-                for (int si = 0; si < D / 16; ++si)
-                    s[kb] = mfma32(*(const bf16x8*)(ks + kofs[si] + kb * 32 * D), qreg[si], s[kb]);
+            for (int si = 0; si < D / 16; ++si) {
+                const bf16x8 k0v = *(const bf16x8*)(ks + kofs[si]);
+                const bf16x8 k1v = *(const bf16x8*)(ks + kofs[si] + 32 * D);
+                s[0] = mfma32(k0v, qreg[si], s[0]);
+                s[1] = mfma32(k1v, qreg[si], s[1]);
             }
+            // K operand reads kept four ahead of the MFMAs that consume them.
+            SCHED_GROUP(kSchedDsRead, 4);
+#pragma unroll
+            for (int i = 0; i < D / 8 - 4; ++i) {
+                SCHED_GROUP(kSchedMfma, 1);
+                SCHED_GROUP(kSchedDsRead, 1);
+            }
+            SCHED_GROUP(kSchedMfma, 4);
             if (MASKED && k0 + BN - 1 > tw_lo) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
@@ -287,7 +307,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
                         if (key > tcol) s[kb][j] = -INFINITY;
                     }
             }
-            softmax_update<D, 2>(s, m, l, o, a.c);
+            softmax_update<D, 2, false>(s, m, l, o, a.c);
+            float ps = 0.f;   // row sum of this tile's weights, as rounded for the PV product
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -296,6 +317,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
                     const bf16x8 pb = to_bf16x8(p[8 * sp + 0], p[8 * sp + 1], p[8 * sp + 2],
                                                 p[8 * sp + 3], p[8 * sp + 4], p[8 * sp + 5],
                                                 p[8 * sp + 6], p[8 * sp + 7]);
+                    ps = row_sum_bf16(pb, ps);
                     const int rowoff = (kb * 32 + 16 * sp) * D;
 #pragma unroll
                     for (int db = 0; db < D / 32; ++db) {
@@ -305,6 +327,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
                         o[db] = mfma32(av, pb, o[db]);
                     }
                 }
+            l += sum_halves(ps);
         }
         wait_vmem();
         __syncthreads();
