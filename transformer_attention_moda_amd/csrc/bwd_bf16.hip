@@ -500,6 +500,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_depth_kernel(BwdArgs a)
     using TL = LdsTile<D>;
     constexpr int BM = NW * 32;
     __shared__ __attribute__((aligned(16))) uint16_t smem[NW][2][32 * TL::PITCH];   // per wave: Q, dO rows
+    __shared__ __attribute__((aligned(16))) uint16_t sout[NW][32 * TL::PITCH];      // per wave: output rows
     __shared__ __attribute__((aligned(16))) float srow[NW][2][32];            // per wave: lse2, D
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -548,18 +549,6 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_depth_kernel(BwdArgs a)
         qreg[si] = lds_chunk<D>(qs, col, 16 * si + 8 * hf);
         dreg[si] = lds_chunk<D>(ds, col, 16 * si + 8 * hf);
     }
-    // Per-register row statistics: register j <-> query row (j/4)*8 + 4*hf + j%4.
-    float lr[16], dr[16];
-    int tr[16];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-        const float4 l4 = *(const float4*)&srow[w][0][jj * 8 + 4 * hf];
-        const float4 d4 = *(const float4*)&srow[w][1][jj * 8 + 4 * hf];
-        lr[4 * jj + 0] = l4.x; lr[4 * jj + 1] = l4.y; lr[4 * jj + 2] = l4.z; lr[4 * jj + 3] = l4.w;
-        dr[4 * jj + 0] = d4.x; dr[4 * jj + 1] = d4.y; dr[4 * jj + 2] = d4.z; dr[4 * jj + 3] = d4.w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) tr[4 * jj + e] = (int)((fw + jj * 8 + 4 * hf + e) >> lgG);
-    }
 
     const float c = a.c;
     const int64_t TL_rows = (int64_t)T * L;
@@ -568,36 +557,61 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_depth_kernel(BwdArgs a)
     uint16_t* dKdb = a.dKd + kvbase * (int64_t)L * D;
     uint16_t* dVdb = a.dVd + kvbase * (int64_t)L * D;
     const int64_t dlo = (int64_t)tw_lo * L, dhi = (int64_t)(tw_hi + 1) * L;
-    for (int64_t rb = dlo; rb < dhi; rb += 32) {
-        const int64_t r = rb + col;                          // this lane's depth row
-        const int64_t rl = min(r, TL_rows - 1);
-        const int rtok = (int)(rl / L);
-        f32x16 s, dp;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) s[j] = dp[j] = 0.f;
+    // Depth K and V rows of block rb as MFMA B operands, loaded one block ahead.
+    bf16x8 kb[2][D / 16], vb[2][D / 16];
+    auto load = [&](int64_t rb, int buf) {
+        const int64_t rl = min(rb + col, TL_rows - 1);
         const uint16_t* krow = Kdb + rl * D + 8 * hf;
         const uint16_t* vrow = Vdb + rl * D + 8 * hf;
 #pragma unroll
         for (int si = 0; si < D / 16; ++si) {
-            s = mfma32(qreg[si], __builtin_bit_cast(bf16x8, ld16(krow + 16 * si)), s);
-            dp = mfma32(dreg[si], __builtin_bit_cast(bf16x8, ld16(vrow + 16 * si)), dp);
+            kb[buf][si] = __builtin_bit_cast(bf16x8, ld16(krow + 16 * si));
+            vb[buf][si] = __builtin_bit_cast(bf16x8, ld16(vrow + 16 * si));
         }
+    };
+    auto block = [&](int64_t rb, const bf16x8 (&kr)[D / 16], const bf16x8 (&vr)[D / 16]) {
+        const int64_t r = rb + col;                          // this lane's depth row
+        const int rtok = (int)(min(r, TL_rows - 1) / L);
+        f32x16 s, dp;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            float p = fast_exp2(fmaf(s[j], c, -lr[j]));
-            if (tr[j] != rtok || r >= dhi) p = 0.f;
-            s[j] = p;
-            dp[j] = p * (dp[j] - dr[j]);
+        for (int j = 0; j < 16; ++j) s[j] = dp[j] = 0.f;
+#pragma unroll
+        for (int si = 0; si < D / 16; ++si) {
+            s = mfma32(qreg[si], kr[si], s);
+            dp = mfma32(dreg[si], vr[si], dp);
+        }
+        // Register j <-> query row (j/4)*8 + 4*hf + j%4; its lse2 and D from the slice.
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const float4 l4 = *(const float4*)&srow[w][0][jj * 8 + 4 * hf];
+            const float4 d4 = *(const float4*)&srow[w][1][jj * 8 + 4 * hf];
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * jj + e;
+                const int tq = (int)((fw + jj * 8 + 4 * hf + e) >> lgG);
+                float p = fast_exp2(fmaf(s[j], c, -lv[e]));
+                if (tq != rtok || r >= dhi) p = 0.f;
+                s[j] = p;
+                dp[j] = p * (dp[j] - dvv[e]);
+            }
         }
         f32x16 gv[D / 32], gk[D / 32];
         zero(gv);
         zero(gk);
         pv_block<D>(ds, 0, s, gv, lane);
         pv_block<D>(qs, 0, dp, gk, lane);
-        if (r < dhi) {
-            store_row_bf16<D>(dVdb + r * D, gv, 1.f, lane);
-            store_row_bf16<D>(dKdb + r * D, gk, a.scale, lane);
-        }
+        const int nrows = (int)min((int64_t)32, dhi - rb);
+        store_rows_bf16<D>(dVdb + rb * D, nrows, gv, 1.f, sout[w], lane);
+        store_rows_bf16<D>(dKdb + rb * D, nrows, gk, a.scale, sout[w], lane);
+    };
+    if (dlo < dhi) load(dlo, 0);
+    for (int64_t rb = dlo; rb < dhi; rb += 64) {
+        if (rb + 32 < dhi) load(rb + 32, 1);
+        block(rb, kb[0], vb[0]);
+        if (rb + 32 >= dhi) break;
+        if (rb + 64 < dhi) load(rb + 64, 0);
+        block(rb + 32, kb[1], vb[1]);
     }
 }
 

@@ -240,6 +240,38 @@ __device__ __forceinline__ void wave_lds_sync()
 __device__ __forceinline__ uint4 ld16(const void* p) { return *(const uint4*)p; }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *(uint4*)p = v; }
 
+// The same D x 32 accumulator (times mul, bf16) as rows [0, nrows) of the 32
+// consecutive rows starting at `rows`, written through `buf` (an LdsTile<D> of 32
+// rows private to the wave) so that the global stores are whole 16-byte chunks,
+// RPI rows (1 KiB) per instruction, instead of 16-byte pieces of 32 rows.
+template <int D>
+__device__ __forceinline__ void store_rows_bf16(uint16_t* rows, int nrows, const f32x16 (&acc)[D / 32],
+                                                float mul, uint16_t* buf, int lane)
+{
+    using TL = LdsTile<D>;
+    const int col = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            bf16x4 v;
+            v[0] = (__bf16)(acc[db][4 * jj + 0] * mul);
+            v[1] = (__bf16)(acc[db][4 * jj + 1] * mul);
+            v[2] = (__bf16)(acc[db][4 * jj + 2] * mul);
+            v[3] = (__bf16)(acc[db][4 * jj + 3] * mul);
+            *(bf16x4*)(buf + TL::off(col, 32 * db + 8 * jj + 4 * hf)) = v;
+        }
+    wave_lds_sync();
+    const int rsub = lane / TL::CPR, c = lane % TL::CPR;
+#pragma unroll
+    for (int k = 0; k < 32 / TL::RPI; ++k) {
+        const int r = k * TL::RPI + rsub;
+        const uint4 v = *(const uint4*)(buf + TL::off(r, 8 * c));
+        if (r < nrows) st16(rows + (int64_t)r * D + 8 * c, v);
+    }
+    wave_lds_sync();
+}
+
 // Workgroup id -> logical work index.  Workgroups are dispatched to the 8 XCDs
 // round-robin (id % 8); this gives XCD x the contiguous logical range
 // [start(x), start(x) + count(x)), so that an XCD's L2 sees the same KV head
