@@ -239,7 +239,7 @@ def test_outputs_stay_inside_their_buffers():
 # ---------------- depth packer ----------------
 
 @pytest.mark.parametrize("shape", [(3, 1, 2, 5, 128), (24, 2, 3, 77, 64), (1, 1, 1, 1, 128),
-                                   (32, 1, 8, 512, 128)])
+                                   (32, 1, 8, 512, 128), (5, 2, 1, 9, 96)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_pack_depth_is_an_exact_transpose(shape, dtype):
     L, B, Hk, T, d = shape
