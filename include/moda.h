@@ -94,7 +94,9 @@ typedef struct {
 moda_status_t moda_fwd(const moda_problem_t* p, const void* Q, const void* K, const void* V,
                        const void* Kd, const void* Vd, void* O, float* lse, void* stream);
 
-/* Bytes of device workspace moda_bwd needs for problem p (0 for an invalid p). */
+/* Bytes of device workspace moda_bwd needs for problem p (0 for an invalid p):
+ * 8 bytes per query row, and for MODA_BF16 with L > 0 another 4*d bytes per
+ * query row (fp32 partial gradients handed between the backward's kernels). */
 size_t moda_bwd_workspace_bytes(const moda_problem_t* p);
 
 /*

@@ -117,11 +117,15 @@ int rows_per_workgroup(const moda_problem_t* p, int G)
     return (int64_t)p->chunk * G >= 256 ? 256 : 128;
 }
 
-// Two fp32 values per query row: the log-sum-exp in log2 units and D = <dO, O>.
-size_t bwd_ws_bytes(const moda::Shape& s)
+// Two fp32 values per query row: the log-sum-exp in log2 units and D = <dO, O>;
+// in bfloat16 with depth rows, then (256-byte aligned) an fp32 row of d values per
+// query row: the depth rows' part of dQ, passed from bwd_depth to bwd_dq.
+size_t bwd_ws_bytes(const moda::Shape& s, int32_t dtype)
 {
     const size_t rows = (size_t)(s.B * s.Hq * s.T);
-    return (2 * rows * sizeof(float) + 255) & ~size_t(255);
+    size_t n = (2 * rows * sizeof(float) + 255) & ~size_t(255);
+    if (dtype == MODA_BF16 && s.L > 0) n += rows * (size_t)s.d * sizeof(float);
+    return (n + 255) & ~size_t(255);
 }
 
 struct Timing {
@@ -222,7 +226,7 @@ size_t moda_bwd_workspace_bytes(const moda_problem_t* p)
 {
     moda::Shape s;
     if (check_problem(p, true, &s) != MODA_OK) return 0;
-    return bwd_ws_bytes(s);
+    return bwd_ws_bytes(s, p->dtype);
 }
 
 moda_status_t moda_bwd(const moda_problem_t* p, const void* Q, const void* K, const void* V,
@@ -242,7 +246,7 @@ moda_status_t moda_bwd(const moda_problem_t* p, const void* Q, const void* K, co
     if (!workspace) return fail(MODA_ERR_INVALID_ARGUMENT, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace) & 255u)
         return fail(MODA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
-    const size_t need = bwd_ws_bytes(s);
+    const size_t need = bwd_ws_bytes(s, p->dtype);
     if (workspace_bytes < need)
         return fail(MODA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu required",
                     workspace_bytes, need);

@@ -9,19 +9,19 @@
 //   dK  = scale sum over queries of dS Q,      dV  = sum over queries of p dO
 //   dKd = scale sum over the token's G heads of dS Q, dVd = same with p dO
 //
-// Four kernels, none with atomics (results are deterministic):
+// Four kernels, in this order, none with atomics (results are deterministic):
 //   bwd_pre    D and lse in log2 units, one per query row (workspace);
+//   bwd_depth  per wave, its tokens' depth rows: S_d = Q Kd^T (lane = depth
+//              row), dVd^T += dO^T P_d, dKd^T += Q^T dS_d, and the depth part of
+//              dQ^T += Kd^T dS_d^T (fp32 rows in the workspace).  A token's G
+//              heads sit in one wave, so every depth row is finished by one wave;
 //   bwd_dq     query-stationary like the forward: per key tile S^T = K Q^T,
 //              dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T with K read
-//              transposed from LDS; then the wave's own depth rows the same
-//              way (depth matching mask);
+//              transposed from LDS; adds the depth part and stores dQ;
 //   bwd_dkdv   key-stationary: each wave keeps 32 keys of K and V as MFMA
 //              operands and walks the query rows that see them:
 //              S = Q K^T, dP = dO V^T (lane = key), dV^T += dO^T P and
-//              dK^T += Q^T dS with dO and Q read transposed from LDS;
-//   bwd_depth  per wave, its tokens' depth rows: S_d = Q Kd^T (lane = depth
-//              row), dVd^T += dO^T P_d, dKd^T += Q^T dS_d.  A token's G heads sit
-//              in one wave, so every depth row is finished by one wave.
+//              dK^T += Q^T dS with dO and Q read transposed from LDS.
 #include <type_traits>
 
 #include "common.hpp"
@@ -46,6 +46,7 @@ struct BwdArgs {
     uint16_t* dVd;
     float* lse2;   // lse * log2(e), [B*Hq*T]
     float* Dv;     // <dO, O>,        [B*Hq*T]
+    float* dqd;    // depth part of dQ / scale, fp32 [B*Hq*T][d] (L > 0)
     int Hq, Hk, T, L, G, lgG;
     int nblocks;   // work blocks per (b, kv) of the launched kernel
     float c;       // scale * log2(e)
@@ -224,42 +225,19 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
         }
     }
 
-    // Depth rows of this wave's tokens: dQ^T += Kd^T dS_d^T.
-    if (L > 0) {
-        uint16_t* kslice = smem + w * 32 * TL::PITCH;
-        const int64_t TL_rows = (int64_t)T * L;
-        const uint16_t* Kdb = a.Kd + kvbase * (int64_t)L * D;
-        const uint16_t* Vdb = a.Vd + kvbase * (int64_t)L * D;
-        const int64_t dlo = (int64_t)tw_lo * L, dhi = (int64_t)(tw_hi + 1) * L;
-        for (int64_t rb = dlo; rb < dhi; rb += 32) {
-            stage_rows<D>(kslice, 32, [&](int r) { return Kdb + min(rb + r, TL_rows - 1) * D; },
-                          lane, 0, 1);
-            f32x16 s, dp;
+    // The depth rows' part (bwd_depth ran before this kernel).
+    if (L > 0 && valid) {
+        const float* drow = a.dqd + qrow_idx * D + 4 * hf;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) s[j] = dp[j] = 0.f;
-            {
-                const int64_t r = min(rb + col, TL_rows - 1);
-                const uint16_t* vrow = Vdb + r * D + 8 * hf;
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                for (int si = 0; si < D / 16; ++si)
-                    dp = mfma32(__builtin_bit_cast(bf16x8, ld16(vrow + 16 * si)), dreg[si], dp);
+            for (int jj = 0; jj < 4; ++jj) {
+                const float4 v = *(const float4*)(drow + 32 * db + 8 * jj);
+                dq[db][4 * jj + 0] += v.x;
+                dq[db][4 * jj + 1] += v.y;
+                dq[db][4 * jj + 2] += v.z;
+                dq[db][4 * jj + 3] += v.w;
             }
-            wait_vmem();
-            wave_lds_sync();
-#pragma unroll
-            for (int si = 0; si < D / 16; ++si)
-                s = mfma32(lds_chunk<D>(kslice, col, 16 * si + 8 * hf), qreg[si], s);
-            const int64_t lo = (int64_t)tcol * L - rb - 4 * hf;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int rj = (j >> 2) * 8 + (j & 3);
-                float p = fast_exp2(fmaf(s[j], c, -lse2));
-                if (rj < lo || rj >= lo + L) p = 0.f;
-                s[j] = p * (dp[j] - Dr);
-            }
-            pv_block<D>(kslice, 0, s, dq, lane);
-            wave_lds_sync();
-        }
     }
     if (valid) store_row_bf16<D>(a.dQ + qrow_idx * D, dq, a.scale, lane);
 }
@@ -500,7 +478,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_depth_kernel(BwdArgs a)
     using TL = LdsTile<D>;
     constexpr int BM = NW * 32;
     __shared__ __attribute__((aligned(16))) uint16_t smem[NW][2][32 * TL::PITCH];   // per wave: Q, dO rows
-    __shared__ __attribute__((aligned(16))) uint16_t sout[NW][32 * TL::PITCH];      // per wave: output rows
+    // per wave: the depth block's Kd rows for the transposed read, then its output rows
+    __shared__ __attribute__((aligned(16))) uint16_t sout[NW][32 * TL::PITCH];
+    constexpr int TP = 36;   // dS_d^T rows (depth rows x 32 queries), padded against bank conflicts
+    __shared__ __attribute__((aligned(16))) uint16_t sds[NW][32 * TP];
     __shared__ __attribute__((aligned(16))) float srow[NW][2][32];            // per wave: lse2, D
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -542,13 +523,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_depth_kernel(BwdArgs a)
     }
     wait_vmem();
     wave_lds_sync();
-    // Query rows as MFMA A operands (lane row l%32, k = d 16*si + 8*hf .. +8).
-    bf16x8 qreg[D / 16], dreg[D / 16];
-#pragma unroll
-    for (int si = 0; si < D / 16; ++si) {
-        qreg[si] = lds_chunk<D>(qs, col, 16 * si + 8 * hf);
-        dreg[si] = lds_chunk<D>(ds, col, 16 * si + 8 * hf);
-    }
+    // Query rows as MFMA A operands (lane row l%32, k = d 16*si + 8*hf .. +8), read from
+    // the slices for every block.
+    LaneOffsets<D> lo;
+    lo.init(lane);
 
     const float c = a.c;
     const int64_t TL_rows = (int64_t)T * L;
@@ -557,8 +535,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_depth_kernel(BwdArgs a)
     uint16_t* dKdb = a.dKd + kvbase * (int64_t)L * D;
     uint16_t* dVdb = a.dVd + kvbase * (int64_t)L * D;
     const int64_t dlo = (int64_t)tw_lo * L, dhi = (int64_t)(tw_hi + 1) * L;
-    // Depth K and V rows of block rb as MFMA B operands, loaded one block ahead.
-    bf16x8 kb[2][D / 16], vb[2][D / 16];
+    // Depth K and V rows of block rb as MFMA B operands.
+    bf16x8 kb[1][D / 16], vb[1][D / 16];
+    f32x16 gq[D / 32];   // dQ^T, depth part, of the wave's 32 query rows
+    zero(gq);
     auto load = [&](int64_t rb, int buf) {
         const int64_t rl = min(rb + col, TL_rows - 1);
         const uint16_t* krow = Kdb + rl * D + 8 * hf;
@@ -577,8 +557,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_depth_kernel(BwdArgs a)
         for (int j = 0; j < 16; ++j) s[j] = dp[j] = 0.f;
 #pragma unroll
         for (int si = 0; si < D / 16; ++si) {
-            s = mfma32(qreg[si], kr[si], s);
-            dp = mfma32(dreg[si], vr[si], dp);
+            s = mfma32(*(const bf16x8*)(qs + lo.a[si]), kr[si], s);
+            dp = mfma32(*(const bf16x8*)(ds + lo.a[si]), vr[si], dp);
         }
         // Register j <-> query row (j/4)*8 + 4*hf + j%4; its lse2 and D from the slice.
 #pragma unroll
@@ -596,6 +576,38 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_depth_kernel(BwdArgs a)
                 dp[j] = p * (dp[j] - dvv[e]);
             }
         }
+        // dQ^T += Kd^T dS_d^T: Kd rows and dS_d (depth row x query) go to LDS, and both
+        // operands come back through transposed reads (k = depth rows 16 sp + 8 (e/4) +
+        // 4 hf + e%4 in both).
+        {
+            uint16_t* kslot = sout[w];
+            uint16_t* tb = sds[w];
+#pragma unroll
+            for (int si = 0; si < D / 16; ++si)
+                *(bf16x8*)(kslot + TL::off(col, 16 * si + 8 * hf)) = kr[si];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const bf16x4 v = {(__bf16)dp[4 * jj + 0], (__bf16)dp[4 * jj + 1], (__bf16)dp[4 * jj + 2],
+                                  (__bf16)dp[4 * jj + 3]};
+                *(bf16x4*)(tb + col * TP + 8 * jj + 4 * hf) = v;
+            }
+            wave_lds_sync();
+            const int krow = 4 * hf + ((col & 15) >> 2), dcol = 16 * (col >> 4) + 4 * (col & 3);
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp) {
+                const bf16x4 b0 = lds_read_tr(tb + (krow + 16 * sp) * TP + dcol);
+                const bf16x4 b1 = lds_read_tr(tb + (krow + 16 * sp + 8) * TP + dcol);
+                const bf16x8 bv = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const bf16x4 a0 = lds_read_tr(kslot + TL::off(krow + 16 * sp, dcol + 32 * db));
+                    const bf16x4 a1 = lds_read_tr(kslot + TL::off(krow + 16 * sp + 8, dcol + 32 * db));
+                    const bf16x8 av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                    gq[db] = mfma32(av, bv, gq[db]);
+                }
+            }
+            wave_lds_sync();
+        }
         f32x16 gv[D / 32], gk[D / 32];
         zero(gv);
         zero(gk);
@@ -605,13 +617,21 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_depth_kernel(BwdArgs a)
         store_rows_bf16<D>(dVdb + rb * D, nrows, gv, 1.f, sout[w], lane);
         store_rows_bf16<D>(dKdb + rb * D, nrows, gk, a.scale, sout[w], lane);
     };
-    if (dlo < dhi) load(dlo, 0);
-    for (int64_t rb = dlo; rb < dhi; rb += 64) {
-        if (rb + 32 < dhi) load(rb + 32, 1);
+    for (int64_t rb = dlo; rb < dhi; rb += 32) {
+        load(rb, 0);
         block(rb, kb[0], vb[0]);
-        if (rb + 32 >= dhi) break;
-        if (rb + 64 < dhi) load(rb + 64, 0);
-        block(rb + 32, kb[1], vb[1]);
+    }
+    // The wave's query rows' depth part of dQ (unscaled, fp32) for bwd_dq: lane column
+    // col is folded row fw + col, register j of block db its element 32 db + (j/4) 8 + 4 hf + j%4.
+    if (fw + col < TG) {
+        const int64_t f = fw + col;
+        float* drow = a.dqd + ((qhead0 + (f & (G - 1))) * T + (f >> lgG)) * D + 4 * hf;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                *(float4*)(drow + 32 * db + 8 * jj) =
+                    make_float4(gq[db][4 * jj + 0], gq[db][4 * jj + 1], gq[db][4 * jj + 2], gq[db][4 * jj + 3]);
     }
 }
 
@@ -627,6 +647,14 @@ hipError_t run(const Shape& s, BwdArgs a, hipStream_t st)
                            dim3(256), 0, st, a);
         timing_end(st);
     }
+    if (s.L > 0) {
+        constexpr int NW = 4;
+        a.nblocks = (int)((TG + NW * 32 - 1) / (NW * 32));
+        timing_begin("bwd_depth", st);
+        hipLaunchKernelGGL((bwd_depth_kernel<D, NW>), dim3((unsigned)(nunits * a.nblocks)),
+                           dim3(NW * 64), 0, st, a);
+        timing_end(st);
+    }
     {
         constexpr int NW = 8;
         a.nblocks = (int)((TG + NW * 32 - 1) / (NW * 32));
@@ -640,14 +668,6 @@ hipError_t run(const Shape& s, BwdArgs a, hipStream_t st)
         a.nblocks = (int)((s.T + NW * 32 - 1) / (NW * 32));
         timing_begin("bwd_dkdv", st);
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW>), dim3((unsigned)(nunits * a.nblocks)),
-                           dim3(NW * 64), 0, st, a);
-        timing_end(st);
-    }
-    if (s.L > 0) {
-        constexpr int NW = 4;
-        a.nblocks = (int)((TG + NW * 32 - 1) / (NW * 32));
-        timing_begin("bwd_depth", st);
-        hipLaunchKernelGGL((bwd_depth_kernel<D, NW>), dim3((unsigned)(nunits * a.nblocks)),
                            dim3(NW * 64), 0, st, a);
         timing_end(st);
     }
@@ -678,6 +698,7 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* Q, const void* K, const v
     a.rows = s.B * s.Hq * s.T;
     a.lse2 = ws;
     a.Dv = ws + a.rows;
+    a.dqd = ws + ((2 * a.rows + 63) & ~int64_t(63));   // 256-byte aligned
     a.Hq = (int)s.Hq;
     a.Hk = (int)s.Hk;
     a.T = (int)s.T;
