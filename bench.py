@@ -171,9 +171,11 @@ def kernel_work(label, w):
     visible (query, key) pairs.  FLOP counts are 2 d per pair and product:
     forward = S and O products over all pairs (4 d); backward = 5 products
     (S recomputed, dP, dV, dK, dQ), of which bwd_dkdv does the four sequence
-    ones besides dQ, bwd_depth the four depth ones, bwd_dq the dQ product
-    (its own S and dP are recomputation).  Memory-bound kernels count the
-    bytes they must move once."""
+    ones besides dQ, bwd_depth all five depth ones, bwd_dq the sequence dQ
+    product (its own S and dP are recomputation).  Memory-bound kernels count
+    the bytes they must move once (bwd_depth: the depth K/V read, their
+    gradients written, the query rows' Q and dO read, and the fp32 depth part
+    of dQ written for bwd_dq)."""
     d, B, Hq, Hk, T, L = w.d, w.B, w.Hq, w.Hk, w.T, w.L
     Ps, Pd = B * Hq * T * (T + 1) / 2, B * Hq * T * L
     q_bytes, dep_bytes, rows = B * Hq * T * d * 2, B * Hk * T * L * d * 2, B * Hq * T
@@ -182,9 +184,9 @@ def kernel_work(label, w):
     if label == "bwd_dkdv":
         return "mfma", 8 * d * Ps, "FLOP"
     if label == "bwd_dq":
-        return "mfma", 2 * d * (Ps + Pd), "FLOP"
+        return "mfma", 2 * d * Ps, "FLOP"
     if label == "bwd_depth":
-        return "hbm", 4 * dep_bytes + 2 * q_bytes + 8 * rows, "B"
+        return "hbm", 4 * dep_bytes + 2 * q_bytes + 8 * rows + (4 * d * rows if L > 0 else 0), "B"
     if label == "bwd_pre":
         return "hbm", 2 * q_bytes + 12 * rows, "B"
     if label == "pack":
