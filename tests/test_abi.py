@@ -93,7 +93,13 @@ def test_fwd_null_depth_rejected_only_when_L_positive():
 def test_workspace_bytes():
     p = prob(B=2, Hq=8, Hk=4, T=100)
     n = mb.moda_bwd_workspace_bytes(p)
-    assert n >= 2 * 8 * 100 * 4 and n % 256 == 0
+    rows = 2 * 8 * 100
+    assert n >= 2 * rows * 4 and n % 256 == 0
+    # bf16 with depth rows also carries an fp32 row of d values per query row
+    assert n >= 2 * rows * 4 + rows * 64 * 4
+    n0 = mb.moda_bwd_workspace_bytes(prob(B=2, Hq=8, Hk=4, T=100, L=0))
+    nf = mb.moda_bwd_workspace_bytes(prob(B=2, Hq=8, Hk=4, T=100, dtype=mb.MODA_F32))
+    assert 2 * rows * 4 <= n0 < 2 * rows * 4 + 256 and n0 == nf
     assert mb.moda_bwd_workspace_bytes(prob(B=0)) == 0
     assert mb.load().moda_bwd_workspace_bytes(None) == 0
 
