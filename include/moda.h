@@ -88,8 +88,10 @@ typedef struct {
  * Kd/Vd with L == 0), a pointer not 16-byte aligned, B, Hq, Hk or T < 1,
  * Hq % Hk != 0, L < 0, a scale that is not finite or not > 0, reserved != 0,
  * chunk < 0, or element counts that overflow int64.  Returns
- * MODA_ERR_UNSUPPORTED for d not in {64, 128}, an unknown dtype, L > MODA_MAX_L
- * or a GQA group size G that does not divide 32.
+ * MODA_ERR_UNSUPPORTED for d not in {64, 128}, an unknown dtype, L > MODA_MAX_L,
+ * a GQA group size G that does not divide 32, T > 2^24, T*max(L, 1) >= 2^31,
+ * B*Hq >= 2^31/64, or ((G-1)*T + 64)*d*2 >= 2^31 (the 32-bit byte offsets with
+ * which the kernels stage a KV group's query rows).
  */
 moda_status_t moda_fwd(const moda_problem_t* p, const void* Q, const void* K, const void* V,
                        const void* Kd, const void* Vd, void* O, float* lse, void* stream);

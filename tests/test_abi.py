@@ -58,6 +58,8 @@ INVALID_PROBLEMS = [
 UNSUPPORTED_PROBLEMS = [
     dict(d=32), dict(d=96), dict(d=256), dict(dtype=7), dict(L=mb.MODA_MAX_L + 1),
     dict(Hq=6, Hk=2), dict(Hq=64, Hk=1), dict(T=(1 << 24) + 1),
+    # staging offsets across a KV group's heads reach (G-1)*T rows: 2 GiB at most
+    dict(Hq=32, Hk=1, T=1 << 20), dict(Hq=2, Hk=1, T=1 << 23, d=128),
 ]
 
 

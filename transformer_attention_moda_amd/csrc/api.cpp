@@ -77,6 +77,12 @@ moda_status_t check_problem(const moda_problem_t* p, bool need_head_dim, moda::S
         return fail(MODA_ERR_UNSUPPORTED, "GQA group size G = %lld must divide 32", (long long)G);
     if (p->T > kMaxT || p->T * (p->L > 0 ? p->L : 1) > kMaxRows || p->B * p->Hq > kMaxRows / 64)
         return fail(MODA_ERR_UNSUPPORTED, "sizes beyond this build's 32-bit row indices");
+    // The backward stages a KV group's query rows (G heads of T rows) with 32-bit byte
+    // offsets from the tile's first row; they reach (G-1)*T + 64 rows.
+    if (((G - 1) * p->T + 64) * p->d * 2 >= (int64_t(1) << 31))
+        return fail(MODA_ERR_UNSUPPORTED,
+                    "(G-1)*T = %lld rows of d = %lld exceed the 2 GiB reach of the staging offsets",
+                    (long long)((G - 1) * p->T), (long long)p->d);
     if (s) {
         s->B = p->B; s->Hq = p->Hq; s->Hk = p->Hk; s->T = p->T; s->d = p->d; s->L = p->L;
         s->scale = p->scale;

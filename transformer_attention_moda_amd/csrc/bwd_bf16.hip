@@ -92,8 +92,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
     constexpr int ELEMS = BN * TL::PITCH;
     static_assert(BN % (TL::RPI * NW) == 0, "tile staging must divide evenly");
     constexpr int BM = NW * 32;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * ELEMS];
-    static_assert(NW * 32 * TL::PITCH <= 2 * 2 * ELEMS, "depth slices must fit");
+    // Per buffer: the K tile, then the V tile.  One array for both buffers: apart, the
+    // compiler keeps more operand addresses live and this kernel spills.
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * ELEMS];
+    uint16_t* const lb0 = smem;
+    uint16_t* const lb1 = smem + 2 * ELEMS;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col = lane & 31, hf = lane >> 5;
@@ -148,29 +151,29 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
     const int t_lo_wg = (int)min(r0 / G, (int64_t)T - 1);
     const int n_full = (t_lo_wg + 1) / BN;     // tiles no wave of this workgroup needs to mask
     auto stage = [&](int tile, uint16_t* ks) {
+        uint16_t* const vs = ks + ELEMS;
         const int k0 = tile * BN;
+        const uint16_t* kt = Kb + (int64_t)k0 * D;
+        const uint16_t* vt = Vb + (int64_t)k0 * D;
         if (k0 + BN <= T) {
-            const uint16_t* kt = Kb + (int64_t)k0 * D;
-            const uint16_t* vt = Vb + (int64_t)k0 * D;
 #pragma unroll
             for (int i2 = 0; i2 < NI; ++i2) {
-                uint16_t* dst = ks + (w + i2 * NW) * TL::RPI * D;
-                __builtin_amdgcn_global_load_lds((glob_void_t*)(kt + sofs[i2]), (lds_void_t*)dst, 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((glob_void_t*)(vt + sofs[i2]), (lds_void_t*)(dst + ELEMS),
-                                                 16, 0, 0);
+                const int o = (w + i2 * NW) * TL::RPI * D;
+                buffer_load_lds16(kt, 2 * sofs[i2], ks + o);
+                buffer_load_lds16(vt, 2 * sofs[i2], vs + o);
             }
         } else {   // the sequence's last tile: rows past T repeat row T-1 (their weights are 0)
-            stage_rows<D>(ks, BN, [&](int r) { return Kb + (int64_t)min(k0 + r, T - 1) * D; }, lane, w, NW);
-            stage_rows<D>(ks + ELEMS, BN, [&](int r) { return Vb + (int64_t)min(k0 + r, T - 1) * D; },
-                          lane, w, NW);
+            auto rowofs = [&](int r) { return (min(k0 + r, T - 1) - k0) * D; };
+            stage_rows<D>(ks, BN, kt, rowofs, lane, w, NW);
+            stage_rows<D>(vs, BN, vt, rowofs, lane, w, NW);
         }
     };
     auto step = [&](auto bufc, auto maskc, int it) {
         constexpr int BUF = decltype(bufc)::value;
         constexpr bool MASKED = decltype(maskc)::value;
-        const uint16_t* ks = smem + 2 * BUF * ELEMS;
+        const uint16_t* ks = BUF ? lb1 : lb0;
         const uint16_t* vs = ks + ELEMS;
-        if (it + 1 < ntiles) stage(it + 1, smem + 2 * (BUF ^ 1) * ELEMS);
+        if (it + 1 < ntiles) stage(it + 1, BUF ? lb0 : lb1);
         const int k0 = it * BN;
         if (!MASKED || k0 <= tw_hi) {
             f32x16 sv[2], dp[2];
@@ -207,7 +210,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
     using I1 = std::integral_constant<int, 1>;
     using BF = std::integral_constant<bool, false>;
     using BT = std::integral_constant<bool, true>;
-    stage(0, smem);
+    stage(0, lb0);
     wait_vmem();
     __syncthreads();
     int it = 0;
@@ -252,9 +255,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
     static_assert(BQ % (TL::RPI * NW) == 0, "tile staging must divide evenly");
     constexpr int BK = NW * 32;   // keys per workgroup
     constexpr int TILE = BQ * D;  // elements of one Q or dO tile
-    // [buf][Q, dO][BQ rows] then [buf][lse2, D][BQ]
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
-    __shared__ __attribute__((aligned(16))) float srow[2][2][BQ];
+    // Per buffer: the Q and dO tiles, then the tiles' lse2 and D rows.  One array per
+    // buffer, so that the compiler can tell a pending load into one buffer from reads of
+    // the other (and keeps a single address register per operand for both tiles).
+    __shared__ __attribute__((aligned(16))) uint16_t lb0[2 * TILE], lb1[2 * TILE];
+    __shared__ __attribute__((aligned(16))) float sr0[2 * BQ], sr1[2 * BQ];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col = lane & 31, hf = lane >> 5;
@@ -300,36 +305,37 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
         sofs[i2] = (int)(((int64_t)(r & (G - 1)) * T + (r >> lgG)) * D) +
                    ((lane % TL::CPR) ^ TL::swz(r)) * 8;
     }
-    const int64_t rofs = (int64_t)(tid & (G - 1)) * T + (tid >> lgG);   // lse/D row offset (tid < BQ)
-    float lst = 0.f, dvst = 0.f;
+    static_assert(BQ == 64, "one wave stages a tile's lse2 and D rows");
+    const uint32_t rofs = 4u * (uint32_t)((lane & (G - 1)) * T + (lane >> lgG));   // lse/D byte offset
     auto qi_of = [&](int64_t f) {
         f = min(f, TG - 1);
         return (qhead0 + (f & (G - 1))) * T + (f >> lgG);
     };
-    auto stage = [&](int tile, uint16_t* qs) {
+    auto stage = [&](int tile, uint16_t* qs, float* sr) {
+        uint16_t* const ds = qs + TILE;
         const int64_t f0 = f_start + (int64_t)tile * BQ;
+        const int64_t base = qhead0 * T + (f0 >> lgG);   // row of folded row f0 (f0 % G == 0)
+        const uint16_t* qt = a.Q + base * D;
+        const uint16_t* dt = a.dO + base * D;
         if (f0 + BQ <= TG) {
-            const int64_t base = qhead0 * T + (f0 >> lgG);
-            const uint16_t* qt = a.Q + base * D;
-            const uint16_t* dt = a.dO + base * D;
 #pragma unroll
             for (int i2 = 0; i2 < NI; ++i2) {
-                uint16_t* dst = qs + (w + i2 * NW) * TL::RPI * D;
-                __builtin_amdgcn_global_load_lds((glob_void_t*)(qt + sofs[i2]), (lds_void_t*)dst, 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((glob_void_t*)(dt + sofs[i2]), (lds_void_t*)(dst + TILE),
-                                                 16, 0, 0);
+                const int o = (w + i2 * NW) * TL::RPI * D;
+                buffer_load_lds16(qt, 2 * sofs[i2], qs + o);
+                buffer_load_lds16(dt, 2 * sofs[i2], ds + o);
             }
-            if (tid < BQ) {
-                lst = a.lse2[base + rofs];
-                dvst = a.Dv[base + rofs];
+            if (w == 0) {
+                buffer_load_lds<4>(a.lse2 + base, rofs, sr);
+                buffer_load_lds<4>(a.Dv + base, rofs, sr + BQ);
             }
         } else {   // the last tile: rows past the end repeat the last row with lse +inf (weight 0)
-            stage_rows<D>(qs, BQ, [&](int r) { return a.Q + qi_of(f0 + r) * D; }, lane, w, NW);
-            stage_rows<D>(qs + TILE, BQ, [&](int r) { return a.dO + qi_of(f0 + r) * D; }, lane, w, NW);
-            if (tid < BQ) {
-                const int64_t f = f0 + tid;
-                lst = f < TG ? a.lse2[qi_of(f)] : INFINITY;
-                dvst = f < TG ? a.Dv[qi_of(f)] : 0.f;
+            auto rowofs = [&](int r) { return (int)(qi_of(f0 + r) - base) * D; };
+            stage_rows<D>(qs, BQ, qt, rowofs, lane, w, NW);
+            stage_rows<D>(ds, BQ, dt, rowofs, lane, w, NW);
+            if (w == 0) {
+                const int64_t f = f0 + lane;
+                sr[lane] = f < TG ? a.lse2[qi_of(f)] : INFINITY;
+                sr[BQ + lane] = f < TG ? a.Dv[qi_of(f)] : 0.f;
             }
         }
     };
@@ -338,9 +344,13 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
     auto step = [&](auto bufc, auto maskc, int it) {
         constexpr int BUF = decltype(bufc)::value;
         constexpr bool MASKED = decltype(maskc)::value;
-        const uint16_t* qs = smem + 2 * BUF * TILE;
+        const uint16_t* qs = BUF ? lb1 : lb0;
         const uint16_t* ds = qs + TILE;
-        if (it + 1 < ntiles) stage(it + 1, smem + 2 * (BUF ^ 1) * TILE);
+        const float* sr = BUF ? sr1 : sr0;
+        if (it + 1 < ntiles) {
+            if (BUF) stage(it + 1, lb0, sr0);
+            else stage(it + 1, lb1, sr1);
+        }
         const int64_t f0 = f_start + (int64_t)it * BQ;
         // Weights of block qb: P = exp2(S c - lse2) (masked), dS = P (dP - D).
         auto weights = [&](int qb, f32x16& sv, f32x16& dp) {
@@ -348,8 +358,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int rbase = qb * 32 + jj * 8 + 4 * hf;
-                const float4 l4 = *(const float4*)&srow[BUF][0][rbase];
-                const float4 d4 = *(const float4*)&srow[BUF][1][rbase];
+                const float4 l4 = *(const float4*)&sr[rbase];
+                const float4 d4 = *(const float4*)&sr[BQ + rbase];
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -430,10 +440,6 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
                 SCHED_GROUP(kSchedDsRead, 2);
             }
         }
-        if (it + 1 < ntiles && tid < BQ) {
-            srow[BUF ^ 1][0][tid] = lst;
-            srow[BUF ^ 1][1][tid] = dvst;
-        }
         wait_vmem();
         __syncthreads();
     };
@@ -443,11 +449,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
     using BF = std::integral_constant<bool, false>;
     using BT = std::integral_constant<bool, true>;
     if (ntiles > 0) {
-        stage(0, smem);
-        if (tid < BQ) {
-            srow[0][0][tid] = lst;
-            srow[0][1][tid] = dvst;
-        }
+        stage(0, lb0, sr0);
     }
     wait_vmem();
     __syncthreads();
@@ -508,8 +510,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_depth_kernel(BwdArgs a)
         f = min(f, TG - 1);
         return (qhead0 + (f & (G - 1))) * T + (f >> lgG);
     };
-    stage_rows<D>(qs, 32, [&](int r) { return a.Q + qi_of(fw + r) * D; }, lane, 0, 1);
-    stage_rows<D>(ds, 32, [&](int r) { return a.dO + qi_of(fw + r) * D; }, lane, 0, 1);
+    {
+        const int64_t q0 = qi_of(fw);   // fw % G == 0, so later rows sit at or after it
+        auto rowofs = [&](int r) { return (int)(qi_of(fw + r) - q0) * D; };
+        stage_rows<D>(qs, 32, a.Q + q0 * D, rowofs, lane, 0, 1);
+        stage_rows<D>(ds, 32, a.dO + q0 * D, rowofs, lane, 0, 1);
+    }
     if (lane < 32) {
         const int64_t f = fw + lane;
         float lv = INFINITY, dvv = 0.f;

@@ -85,18 +85,53 @@ struct LdsTile {
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glob_void_t;
 
-// Stage rows [0, nrows) of an LdsTile<D> with direct 16-byte global->LDS loads
-// (global_load_lds_dwordx4: lane i of a wave writes bytes [16i, 16i+16) of a
-// 1 KiB block).  Each wave instruction fills RPI rows; lane i fetches the
-// logical chunk that belongs at physical chunk i % CPR of its row.  rowptr(r)
-// returns the global address of tile row r (always a valid row).  Waves
-// w, w + nw, ... share the instructions.  The data is in LDS once the issuing
-// wave has waited for its vector-memory counter.
-template <int D, typename RowPtr>
-__device__ __forceinline__ void stage_rows(uint16_t* tile, int nrows, RowPtr rowptr, int lane,
-                                           int w, int nw)
+// The value of p in the first active lane, as a wave-uniform (scalar) pointer.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p)
+{
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (T*)(((uint64_t)hi << 32) | lo);
+}
+
+// Direct global->LDS load of BYTES (4 or 16) per lane (buffer_load_dword[x4] ... lds):
+// lane i reads base + soff + voff (byte offsets: soff wave-uniform, voff per lane, their
+// sum below 2^32) and writes bytes [BYTES*i, BYTES*(i+1)) of the block at lds.  base
+// and lds must be wave-uniform.  The
+// buffer form is used rather than the global one because, while a global-form load
+// into LDS is pending, the compiler's wait-count insertion drains every LDS read
+// (lgkmcnt(0)) and every vector load (vmcnt(0)) it meets; with the buffer form it
+// keeps independent reads in flight and tells apart loads into different __shared__
+// arrays.  The data is in LDS once the issuing wave has waited for its vector-memory
+// counter.
+template <int BYTES>
+__device__ __forceinline__ void buffer_load_lds(const void* base, uint32_t voff, void* lds,
+                                                uint32_t soff = 0)
+{
+    static_assert(BYTES == 4 || BYTES == 16, "direct loads of 4 or 16 bytes per lane");
+    void* b = uniform_ptr(const_cast<void*>(base));
+    auto rsrc = __builtin_amdgcn_make_buffer_rsrc(b, 0, -1, 0x00020000);
+    if constexpr (BYTES == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 4, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t voff, void* lds,
+                                                  uint32_t soff = 0)
+{
+    buffer_load_lds<16>(base, voff, lds, soff);
+}
+
+// Stage rows [0, nrows) of an LdsTile<D> with direct loads.  Each wave instruction
+// fills RPI rows (1 KiB); lane i fetches the logical chunk that belongs at physical
+// chunk i % CPR of its row.  Tile row r is read from base + rowofs(r) elements, with
+// base wave-uniform and 0 <= rowofs(r) < 2^30 - D.  Waves w, w + nw, ... share the
+// instructions.
+template <int D, typename RowOfs>
+__device__ __forceinline__ void stage_rows(uint16_t* tile, int nrows, const uint16_t* base,
+                                           RowOfs rowofs, int lane, int w, int nw)
 {
     using TL = LdsTile<D>;
     const int ninstr = nrows / TL::RPI;
@@ -104,9 +139,7 @@ __device__ __forceinline__ void stage_rows(uint16_t* tile, int nrows, RowPtr row
     for (int k = w; k < ninstr; k += nw) {
         const int r = k * TL::RPI + rsub;
         const int c = p ^ TL::swz(r);
-        const uint16_t* g = rowptr(r) + c * 8;
-        __builtin_amdgcn_global_load_lds((glob_void_t*)g, (lds_void_t*)(tile + k * TL::RPI * D),
-                                         16, 0, 0);
+        buffer_load_lds16(base, 2u * (uint32_t)(rowofs(r) + c * 8), tile + k * TL::RPI * D);
     }
 }
 

@@ -115,10 +115,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
     constexpr int ELEMS = BN * TL::PITCH;      // one K or V tile
     static_assert(BN % (TL::RPI * NW) == 0, "tile staging must divide evenly");
     constexpr int BM = NW * 32;
-    // [buf][K or V][BN rows]; after the sequence loop it holds NW private 32-row
-    // depth slices.
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * ELEMS];
-    static_assert(NW * 32 * TL::PITCH <= 2 * 2 * ELEMS, "depth slices must fit");
+    // Per buffer: the K tile, then the V tile.  One array per buffer, so that the
+    // compiler can tell a pending load into one buffer from reads of the other (and keeps
+    // a single address register per operand for both tiles).  After the sequence loop
+    // they hold NW private 32-row depth slices, four per array.
+    __shared__ __attribute__((aligned(16))) uint16_t lk0[ELEMS], lv0[ELEMS], lk1[ELEMS], lv1[ELEMS];
+    static_assert(ELEMS == 2 * 32 * TL::PITCH && NW <= 8, "depth slices must fit");
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col = lane & 31, hf = lane >> 5;
@@ -178,18 +180,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
         const uint16_t* Vdb = a.Vd + kvbase * (int64_t)L * D;
         const int64_t dlo = (int64_t)tw_lo * L, dhi = (int64_t)(tw_hi + 1) * L;
         const int nblk = (int)((dhi - dlo + 31) / 32);
-        uint16_t* slot = smem + w * 32 * D;
+        uint16_t* const arr = (w >> 1) == 0 ? lk0 : (w >> 1) == 1 ? lv0 : (w >> 1) == 2 ? lk1 : lv1;
+        uint16_t* const slot = arr + (w & 1) * 32 * D;
         constexpr int NK = D / 16;                     // K loads per block (vector-memory instructions)
         bf16x8 kr[D / 16];
-        auto issue_v = [&](int i) {
+        auto issue_v = [&](int i) {   // rows past the end repeat the last row (weight 0)
             const int64_t rb = dlo + 32 * (int64_t)i;
-            if (rb + 32 <= TL_rows) {
-                const uint16_t* vt = Vdb + rb * D;
-                stage_rows<D>(slot, 32, [&](int r) { return vt + r * D; }, lane, 0, 1);
-            } else {
-                stage_rows<D>(slot, 32, [&](int r) { return Vdb + min(rb + r, TL_rows - 1) * D; },
-                              lane, 0, 1);
-            }
+            stage_rows<D>(slot, 32, Vdb + rb * D, [&](int r) { return (int)(min(rb + r, TL_rows - 1) - rb) * D; },
+                          lane, 0, 1);
         };
         auto issue_k = [&](int i) {
             const uint16_t* krow = Kdb + min(dlo + 32 * (int64_t)i + col, TL_rows - 1) * D + 8 * hf;
@@ -252,22 +250,22 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
     const int t_lo_wg = (int)min(r0 / G, (int64_t)T - 1);
     const int n_full = (t_lo_wg + 1) / BN;     // tiles no wave of this workgroup needs to mask
 
-    auto stage = [&](int tile, uint16_t* ks) {
+    auto stage = [&](int tile, uint16_t* ks, uint16_t* vs) {
         const int k0 = tile * BN;
-        if (k0 + BN <= T) {
-            const uint16_t* kt = Kb + (int64_t)k0 * D;
-            const uint16_t* vt = Vb + (int64_t)k0 * D;
+        if (k0 + BN <= T) {   // tile base as the scalar offset: k0*D*2 < 2^32 since T <= 2^24
+            const uint32_t tb = (uint32_t)k0 * (2 * D);
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                uint16_t* dst = ks + (w + i * NW) * TL::RPI * D;
-                __builtin_amdgcn_global_load_lds((glob_void_t*)(kt + sofs[i]), (lds_void_t*)dst, 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((glob_void_t*)(vt + sofs[i]), (lds_void_t*)(dst + ELEMS),
-                                                 16, 0, 0);
+                const int o = (w + i * NW) * TL::RPI * D;
+                buffer_load_lds16(Kb, 2 * sofs[i], ks + o, tb);
+                buffer_load_lds16(Vb, 2 * sofs[i], vs + o, tb);
             }
         } else {   // the sequence's last tile: rows past T repeat row T-1 (their weights are 0)
-            stage_rows<D>(ks, BN, [&](int r) { return Kb + (int64_t)min(k0 + r, T - 1) * D; }, lane, w, NW);
-            stage_rows<D>(ks + ELEMS, BN, [&](int r) { return Vb + (int64_t)min(k0 + r, T - 1) * D; },
-                          lane, w, NW);
+            const uint16_t* kt = Kb + (int64_t)k0 * D;
+            const uint16_t* vt = Vb + (int64_t)k0 * D;
+            auto rowofs = [&](int r) { return (min(k0 + r, T - 1) - k0) * D; };
+            stage_rows<D>(ks, BN, kt, rowofs, lane, w, NW);
+            stage_rows<D>(vs, BN, vt, rowofs, lane, w, NW);
         }
     };
 
@@ -275,9 +273,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
     auto step = [&](auto bufc, auto maskc, int it) {
         constexpr int BUF = decltype(bufc)::value;
         constexpr bool MASKED = decltype(maskc)::value;
-        const uint16_t* ks = smem + 2 * BUF * ELEMS;
-        const uint16_t* vs = ks + ELEMS;
-        if (it + 1 < ntiles) stage(it + 1, smem + 2 * (BUF ^ 1) * ELEMS);
+        const uint16_t* ks = BUF ? lk1 : lk0;
+        const uint16_t* vs = BUF ? lv1 : lv0;
+        if (it + 1 < ntiles) {
+            if (BUF) stage(it + 1, lk0, lv0);
+            else stage(it + 1, lk1, lv1);
+        }
         const int k0 = it * BN;
         if (!MASKED || k0 <= tw_hi) {
             f32x16 s[2];
@@ -337,7 +338,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
     using I1 = std::integral_constant<int, 1>;
     using BF = std::integral_constant<bool, false>;
     using BT = std::integral_constant<bool, true>;
-    stage(0, smem);
+    stage(0, lk0, lv0);
     wait_vmem();
     __syncthreads();
     int it = 0;
