@@ -7,41 +7,40 @@
 // ("Mixture-of-Depths Attention", arXiv 2603.15619, paper summary,
 // "Hardware-Efficient Implementation", natural-layout paragraph and
 // "Flash-compatible depth-KV layout").  The kernel is a bitwise copy bound by
-// HBM bandwidth: every output 16-byte chunk is written once, in order, and
-// every input row is read as whole 16-byte chunks.
+// HBM bandwidth.  Lane i owns 16-byte chunk i of the [B*Hk*T, row] source rows and
+// walks the L layers: for each layer a workgroup reads 256 consecutive chunks (one
+// contiguous span) and writes them as depth row l of their tokens.  Its index
+// division happens once, not per layer; loads and stores are non-temporal (every
+// byte is touched once).
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moda {
 namespace {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int PACK_THREADS = 256;
-constexpr int PACK_UNROLL = 4;
+constexpr int PACK_UNROLL = 8;   // layers in flight per lane
 
-__global__ __launch_bounds__(PACK_THREADS) void pack_kernel(const uint4* __restrict__ in,
-                                                            uint4* __restrict__ out, int64_t L,
-                                                            int64_t BHk, int64_t T, int64_t cpr,
-                                                            int64_t total)
+__global__ __launch_bounds__(PACK_THREADS) void pack_kernel(const u32x4* __restrict__ in,
+                                                            u32x4* __restrict__ out, int L,
+                                                            int64_t chunks, int64_t cpr)
 {
-    // Output chunk o = ((bkv * T + t) * L + l) * cpr + ch.
-    const int64_t stride = (int64_t)gridDim.x * PACK_THREADS * PACK_UNROLL;
-    for (int64_t base = (int64_t)blockIdx.x * PACK_THREADS * PACK_UNROLL + threadIdx.x;
-         base < total; base += stride) {
-        uint4 v[PACK_UNROLL];
-        int64_t oi[PACK_UNROLL];
+    // chunks = B*Hk*T*cpr source chunks per layer; chunk i is chunk i % cpr of row i / cpr.
+    for (int64_t i = (int64_t)blockIdx.x * PACK_THREADS + threadIdx.x; i < chunks;
+         i += (int64_t)gridDim.x * PACK_THREADS) {
+        const int64_t row = i / cpr, ch = i - row * cpr;
+        const u32x4* src = in + i;
+        u32x4* dst = out + row * L * cpr + ch;
+        int l = 0;
+        for (; l + PACK_UNROLL <= L; l += PACK_UNROLL) {
+            u32x4 v[PACK_UNROLL];
 #pragma unroll
-        for (int u = 0; u < PACK_UNROLL; ++u) {
-            const int64_t o = base + (int64_t)u * PACK_THREADS;
-            oi[u] = o;
-            if (o < total) {
-                const int64_t ch = o % cpr, r = o / cpr;
-                const int64_t l = r % L, tt = r / L;         // tt = bkv * T + t
-                v[u] = in[((l * BHk) * T + tt) * cpr + ch];
-            }
+            for (int u = 0; u < PACK_UNROLL; ++u) v[u] = __builtin_nontemporal_load(src + (l + u) * chunks);
+#pragma unroll
+            for (int u = 0; u < PACK_UNROLL; ++u) __builtin_nontemporal_store(v[u], dst + (l + u) * cpr);
         }
-#pragma unroll
-        for (int u = 0; u < PACK_UNROLL; ++u)
-            if (oi[u] < total) out[oi[u]] = v[u];
+        for (; l < L; ++l) __builtin_nontemporal_store(__builtin_nontemporal_load(src + l * chunks), dst + l * cpr);
     }
 }
 
@@ -51,13 +50,12 @@ hipError_t launch_pack_depth(int64_t L, int64_t B, int64_t Hk, int64_t T, int64_
                              const void* layers, void* packed, hipStream_t st)
 {
     const int64_t cpr = row_bytes / 16;
-    const int64_t total = B * Hk * T * L * cpr;
-    const int64_t per_block = (int64_t)PACK_THREADS * PACK_UNROLL;
-    int64_t blocks = (total + per_block - 1) / per_block;
-    if (blocks > 256 * 64) blocks = 256 * 64;
+    const int64_t chunks = B * Hk * T * cpr;
+    int64_t blocks = (chunks + PACK_THREADS - 1) / PACK_THREADS;
+    if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
     timing_begin("pack", st);
     hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(PACK_THREADS), 0, st,
-                       (const uint4*)layers, (uint4*)packed, L, B * Hk, T, cpr, total);
+                       (const u32x4*)layers, (u32x4*)packed, (int)L, chunks, cpr);
     timing_end(st);
     return hipGetLastError();
 }
