@@ -95,6 +95,31 @@ def test_long_64k_forward_sampled_rows():
           lr[:, None], w.dtype)
 
 
+def test_long_64k_backward_sampled_token_ranges():
+    """The timed step's backward at its full size and launch configuration, against exact
+    oracle gradients of three token ranges.  For KV group (b, kv) and tokens [t_lo, t_hi)
+    the oracle's dQ rows and the depth rows' dKd, dVd are complete; with t_hi = T the dK
+    and dV rows at or after t_lo are complete too (only those tokens' queries see them)."""
+    w = W["long_64k"]
+    x = inputs.make(w, seed=6, device=DEV, names=("Q", "K", "V", "Kd", "Vd", "dO"))
+    O, lse = run_fwd(x, w)
+    dQ, dK, dV, dKd, dVd = run_bwd(x, w, O, lse)
+    torch.cuda.synchronize()
+    h = oracle_inputs(x)
+    G, T, L = w.G, w.T, w.L
+    for b, kv, t_lo, t_hi in ((0, 0, T - 40, T), (0, 5, 30000, 30024), (0, 7, 0, 24)):
+        g = oracle.bwd_group(h["Q"], h["K"], h["V"], h["Kd"], h["Vd"], h["dO"], L, w.scale,
+                             b, kv, t_lo, t_hi)
+        hs, ts = slice(kv * G, (kv + 1) * G), slice(t_lo, t_hi)
+        tag = f"{w.name} (b={b}, kv={kv}, tokens {t_lo}..{t_hi - 1})"
+        check(f"{tag} dQ", to64(dQ[b, hs, ts]), g["dQ"], w.dtype)
+        check(f"{tag} dKd", to64(dKd[b, kv, t_lo * L:t_hi * L]), g["dKd"], w.dtype)
+        check(f"{tag} dVd", to64(dVd[b, kv, t_lo * L:t_hi * L]), g["dVd"], w.dtype)
+        if t_hi == T:
+            check(f"{tag} dK", to64(dK[b, kv, t_lo:]), g["dK"][t_lo:], w.dtype)
+            check(f"{tag} dV", to64(dV[b, kv, t_lo:]), g["dV"][t_lo:], w.dtype)
+
+
 def test_train_4k_forward_backward_two_kv_groups():
     w = W["train_4k"]
     x = inputs.make(w, seed=5, device=DEV, names=("Q", "K", "V", "Kd", "Vd", "dO"))
