@@ -98,7 +98,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
     uint16_t* const lb0 = smem;
     uint16_t* const lb1 = smem + 2 * ELEMS;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int col = lane & 31, hf = lane >> 5;
     const int G = a.G, T = a.T, L = a.L;
 
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
     __shared__ __attribute__((aligned(16))) uint16_t lb0[2 * TILE], lb1[2 * TILE];
     __shared__ __attribute__((aligned(16))) float sr0[2 * BQ], sr1[2 * BQ];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int col = lane & 31, hf = lane >> 5;
     const int G = a.G, T = a.T, lgG = a.lgG;
 
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_depth_kernel(BwdArgs a)
     __shared__ __attribute__((aligned(16))) uint16_t sds[NW][32 * TP];
     __shared__ __attribute__((aligned(16))) float srow[NW][2][32];            // per wave: lse2, D
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int col = lane & 31, hf = lane >> 5;
     const int G = a.G, T = a.T, L = a.L, lgG = a.lgG;
 

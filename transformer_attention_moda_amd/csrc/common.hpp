@@ -143,6 +143,11 @@ __device__ __forceinline__ void stage_rows(uint16_t* tile, int nrows, const uint
     }
 }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value: the
+// compiler cannot prove threadIdx.x / 64 uniform, and every per-wave quantity derived
+// from it would otherwise occupy vector registers.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
+
 // Instruction classes for SCHED_GROUP: the compiler's scheduler places the
 // next `count` instructions of the class at this point of the issue order
 // (among those of the enclosing basic block), in program order of the calls.

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
     __shared__ __attribute__((aligned(16))) uint16_t lk0[ELEMS], lv0[ELEMS], lk1[ELEMS], lv1[ELEMS];
     static_assert(ELEMS == 2 * 32 * TL::PITCH && NW <= 8, "depth slices must fit");
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int col = lane & 31, hf = lane >> 5;
     const int G = a.G, T = a.T, L = a.L;
 
