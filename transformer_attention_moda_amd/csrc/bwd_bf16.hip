@@ -187,6 +187,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
                     dp[kb] = mfma32(*(const bf16x8*)(vs + lo.a[si] + kb * 32 * D), dreg[si], dp[kb]);
                 }
             }
+            // K and V operand reads kept 4 ahead of the score MFMAs.
+            SCHED_GROUP(kSchedDsRead, 4);
+#pragma unroll
+            for (int i = 0; i < 2 * D / 8 - 4; ++i) {
+                SCHED_GROUP(kSchedMfma, 1);
+                SCHED_GROUP(kSchedDsRead, 1);
+            }
+            SCHED_GROUP(kSchedMfma, 4);
             const bool need_mask = MASKED && k0 + BN - 1 > tw_lo;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
