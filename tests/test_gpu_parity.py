@@ -120,6 +120,34 @@ def test_long_64k_backward_sampled_token_ranges():
             check(f"{tag} dV", to64(dV[b, kv, t_lo:]), g["dV"][t_lo:], w.dtype)
 
 
+def test_million_token_sequence_sampled():
+    """T = 2^20 tokens (G = 2, d = 64, L = 4), 16 times the bench length: the kernels' row
+    and offset arithmetic far past the five workloads, against sampled forward rows and the
+    oracle's exact gradients of the last 16 tokens (both query heads; all their depth rows,
+    and the dK, dV rows only those tokens' queries see)."""
+    w = inputs.Workload("t1m", B=1, Hq=2, Hk=1, T=1 << 20, d=64, L=4, chunk=0, dtype="bf16")
+    x = inputs.make(w, seed=7, device=DEV, names=("Q", "K", "V", "Kd", "Vd", "dO"))
+    O, lse = run_fwd(x, w)
+    dQ, dK, dV, dKd, dVd = run_bwd(x, w, O, lse)
+    torch.cuda.synchronize()
+    h = oracle_inputs(x)
+    T, L, n = w.T, w.L, 16
+    tokens = [0, 1, 63, 64, 127, 128, 4095, 65535, 65536, (1 << 19) - 1, 1 << 19, T - 2, T - 1]
+    rows = rows_array(1, w.Hq, tokens)
+    Or, lr = oracle.fwd_rows(h["Q"], h["K"], h["V"], h["Kd"], h["Vd"], L, w.scale, rows)
+    check(f"{w.name} O ({len(rows)} sampled rows)", gather_rows(O, rows), Or, w.dtype)
+    check(f"{w.name} lse ({len(rows)} sampled rows)", gather_rows(lse, rows)[:, None],
+          lr[:, None], w.dtype)
+    g = oracle.bwd_group(h["Q"], h["K"], h["V"], h["Kd"], h["Vd"], h["dO"], L, w.scale, 0, 0,
+                         T - n, T)
+    tag = f"{w.name} (tokens {T - n}..{T - 1})"
+    check(f"{tag} dQ", to64(dQ[0, :, T - n:]), g["dQ"], w.dtype)
+    check(f"{tag} dK", to64(dK[0, 0, T - n:]), g["dK"][T - n:], w.dtype)
+    check(f"{tag} dV", to64(dV[0, 0, T - n:]), g["dV"][T - n:], w.dtype)
+    check(f"{tag} dKd", to64(dKd[0, 0, (T - n) * L:]), g["dKd"], w.dtype)
+    check(f"{tag} dVd", to64(dVd[0, 0, (T - n) * L:]), g["dVd"], w.dtype)
+
+
 def test_train_4k_forward_backward_two_kv_groups():
     w = W["train_4k"]
     x = inputs.make(w, seed=5, device=DEV, names=("Q", "K", "V", "Kd", "Vd", "dO"))
