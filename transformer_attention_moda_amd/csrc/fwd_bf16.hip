@@ -115,10 +115,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
     constexpr int ELEMS = BN * TL::PITCH;      // one K or V tile
     static_assert(BN % (TL::RPI * NW) == 0, "tile staging must divide evenly");
     constexpr int BM = NW * 32;
-    // Per buffer: the K tile, then the V tile.  One array per buffer, so that the
-    // compiler can tell a pending load into one buffer from reads of the other (and keeps
-    // a single address register per operand for both tiles).  After the sequence loop
-    // they hold NW private 32-row depth slices, four per array.
+    // K and V tiles of buffers 0 and 1, one array each, so that the compiler can tell a
+    // pending direct load into one buffer from reads of the other.  After the sequence
+    // loop they hold the NW private 32-row depth slices, two per array.
     __shared__ __attribute__((aligned(16))) uint16_t lk0[ELEMS], lv0[ELEMS], lk1[ELEMS], lv1[ELEMS];
     static_assert(ELEMS == 2 * 32 * TL::PITCH && NW <= 8, "depth slices must fit");
 
