@@ -422,7 +422,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
             // arithmetic spread over MFMAs that do not depend on it.
             constexpr int NM = D / 8;   // score MFMAs per block (S and dP)
             constexpr int NG = D / 8;   // gradient MFMAs per block (dV and dK)
-            constexpr int LA = 16, GA = 8;
+            constexpr int LA = 16, GA = 16;
             SCHED_GROUP(kSchedDsRead, LA);
 #pragma unroll
             for (int i = 0; i < 2 * NM - LA; ++i) {
