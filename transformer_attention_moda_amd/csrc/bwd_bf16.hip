@@ -209,6 +209,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
                 }
             pv_block_pre<D>(ks, sv[0], dq, lo);
             pv_block_pre<D>(ks + 32 * D, sv[1], dq, lo);
+            // Transposed K reads of the dQ product kept 4 MFMAs ahead.
+            SCHED_GROUP(kSchedDsRead, 8);
+#pragma unroll
+            for (int i = 0; i < 2 * D / 16 - 4; ++i) {
+                SCHED_GROUP(kSchedMfma, 1);
+                SCHED_GROUP(kSchedDsRead, 2);
+            }
+            SCHED_GROUP(kSchedMfma, 4);
         }
         wait_vmem();
         __syncthreads();
