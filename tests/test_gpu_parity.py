@@ -182,6 +182,9 @@ EDGE = [
     (1, 4, 1, 257, 64, 5),      # G = 4, one past a tile
     (1, 2, 2, 64, 128, 1),      # exactly one tile
     (2, 4, 2, 300, 128, 24),    # chunk boundaries inside tokens of the depth blocks
+    (1, 2, 1, 33, 64, 40),      # a token's depth rows span two 32-row blocks
+    (1, 4, 4, 20, 128, 64),     # G = 1, each token exactly two depth blocks
+    (1, 2, 1, 5, 64, 1024),     # the largest L
 ]
 
 
