@@ -93,7 +93,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
     static_assert(BN % (TL::RPI * NW) == 0, "tile staging must divide evenly");
     constexpr int BM = NW * 32;
     // Per buffer: the K tile, then the V tile.  One array for both buffers: apart, the
-    // compiler keeps more operand addresses live and this kernel spills.
+    // compiler keeps more operand addresses live and this kernel spills (8 registers, about
+    // 4% slower).  The price of one array: the compiler waits for the next tile's load
+    // before the transposed K reads of the dQ product, by when it has mostly landed.
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * ELEMS];
     uint16_t* const lb0 = smem;
     uint16_t* const lb1 = smem + 2 * ELEMS;
