@@ -196,3 +196,12 @@ def bwd(Q, K, V, Kd, Vd, dO, L, scale):
             res["dKd"][b, kv] = r["dKd"]
             res["dVd"][b, kv] = r["dVd"]
     return res
+
+
+def pack_depth(layers):
+    """Layer-major depth KV [L, B, Hk, T, d] -> the token-major layout [B, Hk, T*L, d]
+    in which row t*L + l holds layer l's entry for token t: the "Flash-compatible depth-KV
+    layout" of the paper summary ("Hardware-Efficient Implementation").  A pure index
+    permutation, so the result is bit-exact in any storage type."""
+    L, B, Hk, T, d = layers.shape
+    return np.ascontiguousarray(np.transpose(layers, (1, 2, 3, 0, 4))).reshape(B, Hk, T * L, d)

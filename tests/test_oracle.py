@@ -347,3 +347,21 @@ def test_backward_token_range_restriction():
     np.testing.assert_allclose(part["dV"][t_lo:], full["dV"][0, 1, t_lo:], rtol=0, atol=1e-13)
     np.testing.assert_allclose(part["dKd"], full["dKd"][0, 1, t_lo * L:], rtol=0, atol=1e-13)
     np.testing.assert_allclose(part["dVd"], full["dVd"][0, 1, t_lo * L:], rtol=0, atol=1e-13)
+
+
+def test_pack_depth_row_order_by_explicit_loops():
+    """The packer's layout, element by element: token t's slot l is row t*L + l of its
+    (batch, KV head) block, and nothing else moves (paper summary, flash-compatible
+    depth-KV layout)."""
+    rng = np.random.default_rng(5)
+    for (L, B, Hk, T, d) in [(3, 2, 2, 5, 4), (1, 1, 1, 1, 8), (4, 1, 3, 2, 1)]:
+        layers = rng.integers(0, 1 << 16, size=(L, B, Hk, T, d), dtype=np.uint16)
+        got = oracle.pack_depth(layers)
+        assert got.shape == (B, Hk, T * L, d) and got.dtype == layers.dtype
+        want = np.empty_like(got)
+        for l in range(L):
+            for b in range(B):
+                for h in range(Hk):
+                    for t in range(T):
+                        want[b, h, t * L + l, :] = layers[l, b, h, t, :]
+        assert np.array_equal(got, want)
