@@ -231,13 +231,6 @@ __device__ __forceinline__ void pv_block_pre(const uint16_t* tile, const f32x16&
     }
 }
 
-// The 16-byte MFMA operand chunk (elements 8*c .. 8*c+7) of row `row`.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_chunk(const uint16_t* tile, int row, int elem)
-{
-    return *(const bf16x8*)(tile + LdsTile<D>::off(row, elem));
-}
-
 // Store a D x 32 accumulator held as acc^T blocks (lane column l%32 owns one
 // output row) as bf16 row `row` of out, times `mul`: register j of block db is
 // element 32*db + (j/4)*8 + 4*(l/32) + j%4.
