@@ -15,6 +15,12 @@ folded query matrix and the complete mask matrix exactly as written in
 * one softmax of (Q_fold [K || K_depth]^T) * scale + M, times [V || V_depth]
   (the MoDA equation).
 
+Two variants change only the mask matrix: ``causal=False`` fills the sequence
+block with zeros (every key visible; the MoDA README lists a non-causal kernel
+as future work), and ``window=W`` keeps a depth column visible only if its slot
+j_d mod L is one of the last W (the bounded, sliding-window depth slots of the
+paper summary's section 6, mitigation status).
+
 The backward is the textbook matrix form of a masked softmax-attention
 gradient applied to the same concatenated matrices.  Dense: for tiny inputs
 only (memory grows as (T*G) x (T + T*L)).
@@ -24,7 +30,7 @@ from __future__ import annotations
 import numpy as np
 
 
-def _group(Q, K, V, Kd, Vd, L, b, kv):
+def _group(Q, K, V, Kd, Vd, L, b, kv, causal=True, window=0):
     B, Hq, T, d = Q.shape
     Hk = K.shape[1]
     G = Hq // Hk
@@ -37,8 +43,12 @@ def _group(Q, K, V, Kd, Vd, L, b, kv):
     iq = np.arange(T * G)[:, None]
     ik = np.arange(T)[None, :]
     jd = np.arange(T * L)[None, :]
-    m_seq = np.where(iq // G >= ik, 0.0, -np.inf)
-    m_dep = np.where(iq // G == jd // L, 0.0, -np.inf) if L > 0 else np.zeros((T * G, 0))
+    m_seq = np.where(iq // G >= ik, 0.0, -np.inf) if causal else np.zeros((T * G, T))
+    W = window if window > 0 else L
+    if L > 0:
+        m_dep = np.where((iq // G == jd // L) & (jd % L >= L - W), 0.0, -np.inf)
+    else:
+        m_dep = np.zeros((T * G, 0))
     M = np.concatenate([m_seq, m_dep], axis=1)
     return Qf, keys, vals, M, G, T
 
@@ -48,7 +58,7 @@ def _unfold(x, G, T):
     return np.swapaxes(x.reshape((T, G) + x.shape[1:]), 0, 1)
 
 
-def forward(Q, K, V, Kd, Vd, L, scale):
+def forward(Q, K, V, Kd, Vd, L, scale, causal=True, window=0):
     """O [B,Hq,T,d], lse [B,Hq,T] (float64) from float64 inputs."""
     B, Hq, T, d = Q.shape
     Hk = K.shape[1]
@@ -57,7 +67,7 @@ def forward(Q, K, V, Kd, Vd, L, scale):
     lse = np.zeros((B, Hq, T))
     for b in range(B):
         for kv in range(Hk):
-            Qf, keys, vals, M, G, T = _group(Q, K, V, Kd, Vd, L, b, kv)
+            Qf, keys, vals, M, G, T = _group(Q, K, V, Kd, Vd, L, b, kv, causal, window)
             S = (Qf @ keys.T) * scale + M
             m = S.max(axis=1, keepdims=True)
             E = np.exp(S - m)
@@ -68,7 +78,7 @@ def forward(Q, K, V, Kd, Vd, L, scale):
     return O, lse
 
 
-def backward(Q, K, V, Kd, Vd, dO, L, scale):
+def backward(Q, K, V, Kd, Vd, dO, L, scale, causal=True, window=0):
     """dQ, dK, dV, dKd, dVd (float64) from float64 inputs."""
     B, Hq, T, d = Q.shape
     Hk = K.shape[1]
@@ -80,7 +90,7 @@ def backward(Q, K, V, Kd, Vd, dO, L, scale):
     dVd = np.zeros((B, Hk, T * L, d))
     for b in range(B):
         for kv in range(Hk):
-            Qf, keys, vals, M, G, T = _group(Q, K, V, Kd, Vd, L, b, kv)
+            Qf, keys, vals, M, G, T = _group(Q, K, V, Kd, Vd, L, b, kv, causal, window)
             dOf = np.transpose(dO[b, kv * G:(kv + 1) * G], (1, 0, 2)).reshape(T * G, d)
             S = (Qf @ keys.T) * scale + M
             E = np.exp(S - S.max(axis=1, keepdims=True))

@@ -39,6 +39,17 @@
  *   dQ   = scale (sum_j ds_j K_j + sum_l du_l Kd_{t,l})
  *   dK_j += scale ds_j Q,  dV_j += p_j dO,  dKd_{t,l} += scale du_l Q,  dVd_{t,l} += q_l dO
  *
+ * Two variants of the masks, both readings of open items on the pages:
+ *   - non-causal (flag bit 0): every sequence key 0 .. T-1 is visible to every
+ *     query; the depth matching mask is unchanged.  The MoDA README lists a
+ *     non-causal kernel as future work without defining it; dropping the
+ *     sequence causal mask and keeping the depth one is the plain reading.
+ *   - depth window W (0 < W <= L; 0 means L): a token sees only the last W of
+ *     its L depth slots, rows t*L + L-W .. t*L + L-1.  The paper summary's
+ *     section 6 ("Limitations and Trade-offs", mitigation status) sketches
+ *     bounded depth-KV slots with a sliding-window recency policy; slots are in
+ *     layer order, so the last W are the most recent layers.
+ *
  * Element storage codes: 0 = bf16 (raw 16-bit patterns, upcast exactly),
  * 1 = fp32, 2 = fp64.  All arithmetic is fp64.
  */
@@ -50,9 +61,22 @@
 typedef struct {
     int64_t B, Hq, Hk, T, d, L;
     double scale;
-    int32_t dtype; /* storage code of Q, K, V, K_depth, V_depth, dO */
-    int32_t pad_;
+    int32_t dtype;    /* storage code of Q, K, V, K_depth, V_depth, dO */
+    int32_t flags;    /* bit 0: non-causal */
+    int64_t window;   /* visible depth slots per token (the last ones); 0 = all L */
 } oracle_shape;
+
+/* Last sequence key visible to the query at token t. */
+static int64_t last_key(const oracle_shape* s, int64_t t)
+{
+    return (s->flags & 1) ? s->T - 1 : t;
+}
+
+/* First visible depth slot of a token (slots first_slot .. L-1 are visible). */
+static int64_t first_slot(const oracle_shape* s)
+{
+    return s->window > 0 ? s->L - s->window : 0;
+}
 
 static double elem(const void* p, int dtype, int64_t i)
 {
@@ -87,9 +111,10 @@ static double dot(const oracle_shape* s, const void* x, int64_t xo, const void* 
 }
 
 /*
- * One query row (b, h, t): its t+1 visible sequence scores and its L depth
- * scores, one softmax over their concatenation, the output row and the
- * log-sum-exp.  `scores` is caller scratch of length T+L.
+ * One query row (b, h, t): its visible sequence scores (keys 0 .. last_key)
+ * and its visible depth scores (slots first_slot .. L-1 of token t), one
+ * softmax over their concatenation, the output row and the log-sum-exp.
+ * `scores` is caller scratch of length T+L.
  */
 static void row_forward(const oracle_shape* s, const void* Q, const void* K, const void* V,
                         const void* Kd, const void* Vd, int64_t b, int64_t h, int64_t t,
@@ -97,14 +122,14 @@ static void row_forward(const oracle_shape* s, const void* Q, const void* K, con
 {
     const int64_t G = s->Hq / s->Hk, kv = h / G, L = s->L, d = s->d;
     const int64_t qo = q_off(s, b, h, t);
-    const int64_t nseq = t + 1;
+    const int64_t nseq = last_key(s, t) + 1, l0 = first_slot(s);
     /* pass 1: scores and their maximum */
     double m = -INFINITY;
     for (int64_t j = 0; j < nseq; ++j) {
         scores[j] = s->scale * dot(s, Q, qo, K, kv_off(s, b, kv, j));
         if (scores[j] > m) m = scores[j];
     }
-    for (int64_t l = 0; l < L; ++l) {
+    for (int64_t l = l0; l < L; ++l) {
         scores[nseq + l] = s->scale * dot(s, Q, qo, Kd, dep_off(s, b, kv, t * L + l));
         if (scores[nseq + l] > m) m = scores[nseq + l];
     }
@@ -117,7 +142,7 @@ static void row_forward(const oracle_shape* s, const void* Q, const void* K, con
         Z += w;
         for (int64_t e = 0; e < d; ++e) o[e] += w * elem(V, s->dtype, vo + e);
     }
-    for (int64_t l = 0; l < L; ++l) {
+    for (int64_t l = l0; l < L; ++l) {
         const double w = exp(scores[nseq + l] - m);
         const int64_t vo = dep_off(s, b, kv, t * L + l);
         Z += w;
@@ -130,7 +155,8 @@ static void row_forward(const oracle_shape* s, const void* Q, const void* K, con
 static int shape_ok(const oracle_shape* s)
 {
     return s && s->B > 0 && s->Hq > 0 && s->Hk > 0 && s->T > 0 && s->d > 0 && s->L >= 0 &&
-           s->Hq % s->Hk == 0 && s->dtype >= 0 && s->dtype <= 2;
+           s->Hq % s->Hk == 0 && s->dtype >= 0 && s->dtype <= 2 && (s->flags & ~1) == 0 &&
+           s->window >= 0 && s->window <= s->L;
 }
 
 /*
@@ -166,27 +192,30 @@ int oracle_fwd_rows(const oracle_shape* s, const void* Q, const void* K, const v
 }
 
 /*
- * Backward restricted to the query rows of one KV group: batch b, KV head kv,
- * its G query heads h = kv*G + g, and tokens t in [t_lo, t_hi).  Every output
- * holds exactly the contribution of those rows:
- *   dQ  [G, t_hi-t_lo, d]        gradient rows of those queries (complete)
- *   dK, dV [t_hi, d]             sum over those rows for keys 0 .. t_hi-1
- *   dKd, dVd [(t_hi-t_lo)*L, d]  depth rows of tokens t_lo .. t_hi-1 (complete)
- *   O [G, t_hi-t_lo, d], lse [G, t_hi-t_lo]   the forward rows (by-products)
- * With t_lo = 0 and t_hi = T this is the full gradient of the group.  With
- * t_hi = T, dK/dV rows j >= t_lo are complete too, since only queries at
- * tokens >= j see key j.
+ * Backward restricted to the query rows of one KV group at a set of tokens:
+ * batch b, KV head kv, its G query heads h = kv*G + g, and the n distinct
+ * tokens tok[0..n-1].  Every output holds exactly the contribution of those
+ * rows:
+ *   dQ  [G, n, d]         gradient rows of those queries (complete)
+ *   dK, dV [T, d]         for every key, the sum over those rows that see it
+ *   dKd, dVd [n*L, d]     the L depth rows of each selected token, in the order
+ *                         of tok (complete: only that token's rows see them)
+ *   O [G, n, d], lse [G, n]   the forward rows (by-products)
+ * A row's contribution to dK, dV is scale*ds*Q and p*dO with ds = p (<dO,v> - D),
+ * D = <dO, O>; both vanish when dO is zero at that row.  So when the upstream
+ * gradient is zero at every other token of the group, dK and dV here are the
+ * group's complete gradients.
  * dO has the storage code of the inputs.  Returns 0, or -1 on bad arguments.
  */
-int oracle_bwd_group(const oracle_shape* s, int64_t b, int64_t kv, int64_t t_lo, int64_t t_hi,
-                     const void* Q, const void* K, const void* V, const void* Kd, const void* Vd,
-                     const void* dO, double* dQ, double* dK, double* dV, double* dKd, double* dVd,
-                     double* O, double* lse)
+int oracle_bwd_tokens(const oracle_shape* s, int64_t b, int64_t kv, int64_t n,
+                      const int64_t* tok, const void* Q, const void* K, const void* V,
+                      const void* Kd, const void* Vd, const void* dO, double* dQ, double* dK,
+                      double* dV, double* dKd, double* dVd, double* O, double* lse)
 {
-    if (!shape_ok(s) || b < 0 || b >= s->B || kv < 0 || kv >= s->Hk || t_lo < 0 ||
-        t_hi > s->T || t_lo >= t_hi)
-        return -1;
-    const int64_t G = s->Hq / s->Hk, L = s->L, d = s->d, n = t_hi - t_lo;
+    if (!shape_ok(s) || b < 0 || b >= s->B || kv < 0 || kv >= s->Hk || n < 1) return -1;
+    for (int64_t i = 0; i < n; ++i)
+        if (tok[i] < 0 || tok[i] >= s->T) return -1;
+    const int64_t G = s->Hq / s->Hk, L = s->L, d = s->d, l0 = first_slot(s);
     double* D = (double*)malloc(sizeof(double) * (size_t)(G * n));
     if (!D) return -1;
     int bad = 0;
@@ -201,7 +230,7 @@ int oracle_bwd_group(const oracle_shape* s, int64_t b, int64_t kv, int64_t t_lo,
         } else {
 #pragma omp for schedule(dynamic, 4)
             for (int64_t i = 0; i < G * n; ++i) {
-                const int64_t g = i / n, t = t_lo + i % n, h = kv * G + g;
+                const int64_t g = i / n, t = tok[i % n], h = kv * G + g;
                 double* o = O + i * d;
                 row_forward(s, Q, K, V, Kd, Vd, b, h, t, scores, o, lse + i);
                 double acc = 0.0;
@@ -217,25 +246,26 @@ int oracle_bwd_group(const oracle_shape* s, int64_t b, int64_t kv, int64_t t_lo,
         return -1;
     }
 
-    /* Step 2: per token, dQ of its G rows and the gradients of its own L depth
-     * rows (only that token's G query rows see them). */
+    /* Step 2: per token, dQ of its G rows and the gradients of its own depth rows
+     * (only that token's G query rows see them; slots before first_slot are not
+     * visible and get zero gradient). */
     memset(dKd, 0, sizeof(double) * (size_t)(n * L * d));
     memset(dVd, 0, sizeof(double) * (size_t)(n * L * d));
 #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t tt = 0; tt < n; ++tt) {
-        const int64_t t = t_lo + tt;
+        const int64_t t = tok[tt];
         for (int64_t g = 0; g < G; ++g) {
             const int64_t h = kv * G + g, i = g * n + tt, qo = q_off(s, b, h, t);
             double* dq = dQ + i * d;
             for (int64_t e = 0; e < d; ++e) dq[e] = 0.0;
-            for (int64_t j = 0; j <= t; ++j) {
+            for (int64_t j = 0; j <= last_key(s, t); ++j) {
                 const int64_t ko = kv_off(s, b, kv, j);
                 const double sc = s->scale * dot(s, Q, qo, K, ko);
                 const double p = exp(sc - lse[i]);
                 const double ds = p * (dot(s, dO, qo, V, ko) - D[i]);
                 for (int64_t e = 0; e < d; ++e) dq[e] += s->scale * ds * elem(K, s->dtype, ko + e);
             }
-            for (int64_t l = 0; l < L; ++l) {
+            for (int64_t l = l0; l < L; ++l) {
                 const int64_t ro = dep_off(s, b, kv, t * L + l);
                 const double u = s->scale * dot(s, Q, qo, Kd, ro);
                 const double q = exp(u - lse[i]);
@@ -253,16 +283,16 @@ int oracle_bwd_group(const oracle_shape* s, int64_t b, int64_t kv, int64_t t_lo,
 
     /* Step 3: per sequence key j, the sum over the selected rows that see it. */
 #pragma omp parallel for schedule(dynamic, 16)
-    for (int64_t j = 0; j < t_hi; ++j) {
+    for (int64_t j = 0; j < s->T; ++j) {
         const int64_t ko = kv_off(s, b, kv, j);
         double* dk = dK + j * d;
         double* dv = dV + j * d;
         for (int64_t e = 0; e < d; ++e) dk[e] = dv[e] = 0.0;
-        const int64_t t0 = j > t_lo ? j : t_lo;
-        for (int64_t g = 0; g < G; ++g) {
-            const int64_t h = kv * G + g;
-            for (int64_t t = t0; t < t_hi; ++t) {
-                const int64_t i = g * n + (t - t_lo), qo = q_off(s, b, h, t);
+        for (int64_t tt = 0; tt < n; ++tt) {
+            const int64_t t = tok[tt];
+            if (j > last_key(s, t)) continue;
+            for (int64_t g = 0; g < G; ++g) {
+                const int64_t h = kv * G + g, i = g * n + tt, qo = q_off(s, b, h, t);
                 const double sc = s->scale * dot(s, Q, qo, K, ko);
                 const double p = exp(sc - lse[i]);
                 const double ds = p * (dot(s, dO, qo, V, ko) - D[i]);

@@ -365,3 +365,173 @@ def test_pack_depth_row_order_by_explicit_loops():
                     for t in range(T):
                         want[b, h, t * L + l, :] = layers[l, b, h, t, :]
         assert np.array_equal(got, want)
+
+
+# --- variants: non-causal sequence keys, sliding-window depth slots ---
+
+def test_variants_match_dense_transcription_grid():
+    """Non-causal (the MoDA README's future-work kernel, read as: drop the sequence causal
+    mask, keep the depth matching mask) and the depth window (paper summary, section 6,
+    bounded depth-KV slots with a sliding-window recency policy: the last W slots), fwd
+    and bwd, against the literal mask matrix of oracle/brute.py."""
+    rng = np.random.default_rng(21)
+    for T, L, G, causal in itertools.product((1, 3, 8, 13), (0, 1, 3, 5), (1, 2, 4),
+                                             (True, False)):
+        for W in sorted({0, 1, L} | ({L - 1} if L > 1 else set())):
+            if W > L:
+                continue
+            args = draw(rng, 1, 2 * G, 2, T, 4, L)
+            dO = rng.standard_normal(args[0].shape)
+            tag = f"T{T} L{L} G{G} causal={causal} W={W}"
+            O, lse = oracle.fwd(*args, L, 0.45, causal=causal, window=W)
+            Ob, lb = brute.forward(*args, L, 0.45, causal=causal, window=W)
+            np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12, err_msg=tag)
+            np.testing.assert_allclose(lse, lb, rtol=0, atol=1e-12, err_msg=tag)
+            g = oracle.bwd(*args, dO, L, 0.45, causal=causal, window=W)
+            ref = brute.backward(*args, dO, L, 0.45, causal=causal, window=W)
+            for name, r in zip(("dQ", "dK", "dV", "dKd", "dVd"), ref):
+                np.testing.assert_allclose(g[name], r, rtol=0, atol=1e-11, err_msg=f"{tag} {name}")
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_noncausal_no_depth_equals_library_attention(G):
+    """With L = 0 the non-causal operator is plain bidirectional GQA attention: torch's
+    scaled_dot_product_attention without the causal mask, forward and autograd."""
+    rng = np.random.default_rng(22)
+    Hk, T, d = 2, 17, 8
+    Q, K, V, _, _ = draw(rng, 1, G * Hk, Hk, T, d, 0)
+    dO = rng.standard_normal(Q.shape)
+    O, lse = oracle.fwd(Q, K, V, None, None, 0, 0.3, causal=False)
+    g = oracle.bwd(Q, K, V, None, None, dO, 0, 0.3, causal=False)
+    q, k, v = (torch.from_numpy(x).requires_grad_() for x in (Q, K, V))
+    kr, vr = k.repeat_interleave(G, 1), v.repeat_interleave(G, 1)
+    o = torch.nn.functional.scaled_dot_product_attention(q, kr, vr, is_causal=False, scale=0.3)
+    o.backward(torch.from_numpy(dO))
+    ref_lse = torch.logsumexp(0.3 * q.detach() @ kr.detach().transpose(-1, -2), -1)
+    np.testing.assert_allclose(O, o.detach().numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g["dQ"], q.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g["dK"], k.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g["dV"], v.grad.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("W", [1, 3, 5])
+def test_window_equals_operator_on_truncated_depth_cache(causal, W):
+    """Seeing only the last W of L slots is the plain operator on a depth cache that
+    holds just those W slots per token (L' = W); the hidden slots get zero gradient.
+    W = L is the plain operator itself."""
+    rng = np.random.default_rng(23)
+    B, G, Hk, T, d, L = 1, 2, 2, 11, 6, 5
+    Q, K, V, Kd, Vd = draw(rng, B, G * Hk, Hk, T, d, L)
+    dO = rng.standard_normal(Q.shape)
+    keep = (np.arange(T)[:, None] * L + np.arange(L - W, L)[None, :]).ravel()
+    Kt, Vt = Kd[:, :, keep], Vd[:, :, keep]
+    O, lse = oracle.fwd(Q, K, V, Kd, Vd, L, 0.4, causal=causal, window=W)
+    Ot, lt = oracle.fwd(Q, K, V, Kt, Vt, W, 0.4, causal=causal)
+    np.testing.assert_allclose(O, Ot, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, lt, rtol=0, atol=1e-13)
+    g = oracle.bwd(Q, K, V, Kd, Vd, dO, L, 0.4, causal=causal, window=W)
+    gt = oracle.bwd(Q, K, V, Kt, Vt, dO, W, 0.4, causal=causal)
+    for k in ("dQ", "dK", "dV"):
+        np.testing.assert_allclose(g[k], gt[k], rtol=0, atol=1e-12)
+    for k in ("dKd", "dVd"):
+        np.testing.assert_allclose(g[k][:, :, keep], gt[k], rtol=0, atol=1e-12)
+        hidden = np.ones(T * L, bool)
+        hidden[keep] = False
+        assert np.all(g[k][:, :, hidden] == 0.0)
+
+
+def test_variant_backward_matches_central_finite_differences():
+    rng = np.random.default_rng(24)
+    B, G, Hk, T, d, L, scale = 1, 2, 1, 5, 3, 3, 0.6
+    args = list(draw(rng, B, G * Hk, Hk, T, d, L))
+    dO = rng.standard_normal(args[0].shape)
+    for causal, W in ((False, 0), (True, 2), (False, 1)):
+        g = oracle.bwd(*args, dO, L, scale, causal=causal, window=W)
+        h = 1e-6
+        for ti, name in enumerate(("dQ", "dK", "dV", "dKd", "dVd")):
+            x = args[ti]
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                old = x[idx]
+                x[idx] = old + h
+                lp = float((oracle.fwd(*args, L, scale, causal, W)[0] * dO).sum())
+                x[idx] = old - h
+                lm = float((oracle.fwd(*args, L, scale, causal, W)[0] * dO).sum())
+                x[idx] = old
+                num[idx] = (lp - lm) / (2 * h)
+            err = np.linalg.norm(g[name] - num) / max(np.linalg.norm(num), 1e-300)
+            assert err < 1e-6 or np.linalg.norm(g[name] - num) < 1e-9, (causal, W, name, err)
+
+
+# --- the token-set backward: complete key gradients under a sparse upstream gradient ---
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_sparse_upstream_gradient_token_set_backward_is_complete(causal):
+    """Rows whose upstream gradient is zero contribute nothing to dK and dV (their dS and
+    p*dO vanish), so with dO zero outside a token set the restricted backward over that set
+    gives the complete key gradients; its dQ rows and the set's depth rows are complete in
+    any case."""
+    rng = np.random.default_rng(25)
+    B, G, Hk, T, d, L = 1, 2, 2, 19, 5, 3
+    Q, K, V, Kd, Vd = draw(rng, B, G * Hk, Hk, T, d, L)
+    tokens = np.array([17, 0, 9, 4, 18])           # any order
+    dO = np.zeros(Q.shape)
+    dO[:, :, tokens] = rng.standard_normal((B, G * Hk, len(tokens), d))
+    full = oracle.bwd(Q, K, V, Kd, Vd, dO, L, 0.5, causal=causal, window=2)
+    for kv in range(Hk):
+        part = oracle.bwd_tokens(Q, K, V, Kd, Vd, dO, L, 0.5, 0, kv, tokens, causal=causal,
+                                 window=2)
+        np.testing.assert_allclose(part["dK"], full["dK"][0, kv], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(part["dV"], full["dV"][0, kv], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(part["dQ"], full["dQ"][0, kv * G:(kv + 1) * G][:, tokens],
+                                   rtol=0, atol=1e-13)
+        rows = (tokens[:, None] * L + np.arange(L)[None, :]).ravel()
+        np.testing.assert_allclose(part["dKd"], full["dKd"][0, kv, rows], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(part["dVd"], full["dVd"][0, kv, rows], rtol=0, atol=1e-13)
+
+
+# --- decoding and the append-mode depth cache ---
+
+def test_decode_is_the_forward_row_of_the_new_token():
+    """Decoding one token (paper summary, complexity analysis: one new token attends over
+    the cached sequence keys and its own depth keys) is the forward's row at that token:
+    the dense transcription's last row of the sequence that ends with it.  Cache entries
+    past the token's position must not matter."""
+    rng = np.random.default_rng(26)
+    B, G, Hk, Tcap, d, L = 2, 4, 2, 12, 8, 3
+    _, K, V, Kd, Vd = draw(rng, B, G * Hk, Hk, Tcap, d, L)
+    q = rng.standard_normal((B, G * Hk, d))
+    for pos, W in ((0, 0), (5, 2), (Tcap - 1, 0)):
+        O, lse = oracle.decode(q, K, V, Kd, Vd, L, 0.35, pos, window=W)
+        n = pos + 1
+        Qs = rng.standard_normal((B, G * Hk, n, d))
+        Qs[:, :, pos] = q
+        Ob, lb = brute.forward(Qs, K[:, :, :n], V[:, :, :n], Kd[:, :, :n * L], Vd[:, :, :n * L],
+                               L, 0.35, window=W)
+        np.testing.assert_allclose(O, Ob[:, :, pos], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, lb[:, :, pos], rtol=0, atol=1e-12)
+
+
+def test_depth_append_builds_the_packed_cache():
+    """Appending layer l's entries into slot l for l = 0..L-1 gives exactly the packed
+    token-major layout (pack_depth of the stacked layers); a ranged append writes only
+    rows (t0+i)*L + slot, by explicit loops."""
+    rng = np.random.default_rng(27)
+    L, B, Hk, T, d = 4, 2, 3, 6, 8
+    layers = rng.integers(0, 1 << 16, size=(L, B, Hk, T, d), dtype=np.uint16)
+    cache = np.zeros((B, Hk, T * L, d), np.uint16)
+    for l in range(L):
+        cache = oracle.depth_append(cache, layers[l], L, l)
+    assert np.array_equal(cache, oracle.pack_depth(layers))
+    new = rng.integers(0, 1 << 16, size=(B, Hk, 2, d), dtype=np.uint16)
+    got = oracle.depth_append(cache, new, L, 1, t0=3)
+    want = cache.copy()
+    for b in range(B):
+        for h in range(Hk):
+            for i in range(2):
+                want[b, h, (3 + i) * L + 1, :] = new[b, h, i, :]
+    assert np.array_equal(got, want)
+    with pytest.raises(ValueError):
+        oracle.depth_append(cache, new, L, 1, t0=5)

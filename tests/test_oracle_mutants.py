@@ -16,7 +16,8 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "moda_oracle.c")
 
 MUTANTS = {
     # causal diagonal dropped: key j = t no longer visible
-    "diagonal_excluded": ("const int64_t nseq = t + 1;", "const int64_t nseq = t;"),
+    "diagonal_excluded": ("return (s->flags & 1) ? s->T - 1 : t;",
+                          "return (s->flags & 1) ? s->T - 1 : t - 1;"),
     # KV head chosen by modulo instead of adjacent grouping
     "head_mapping_modulo": ("kv = h / G, L = s->L", "kv = h % s->Hk, L = s->L"),
     # depth rows read layer-major instead of token-major
@@ -46,10 +47,20 @@ MUTANTS = {
     # depth value gradient attributed to the wrong token's rows
     "dVd_wrong_row": ("double* dvd = dVd + (tt * L + l) * d;",
                       "double* dvd = dVd + (((tt + 1) % n) * L + l) * d;"),
+    # non-causal flag ignored: the sequence causal mask stays on
+    "noncausal_keeps_mask": ("return (s->flags & 1) ? s->T - 1 : t;", "return t;"),
+    # depth window ignored: every slot stays visible
+    "window_ignored": ("return s->window > 0 ? s->L - s->window : 0;", "return 0;"),
+    # depth window one slot short
+    "window_off_by_one": ("return s->window > 0 ? s->L - s->window : 0;",
+                          "return s->window > 0 ? s->L - s->window + 1 : 0;"),
+    # key gradients of the token-set backward keep the causal test in non-causal mode
+    "dK_causal_in_noncausal": ("if (j > last_key(s, t)) continue;", "if (j > t) continue;"),
 }
 
 PINS = [
     pins.test_forward_matches_dense_transcription_grid,
+    pins.test_variants_match_dense_transcription_grid,
     pins.test_zero_query_gives_uniform_weights,
     pins.test_hand_worked_two_token_example,
     pins.test_sequence_pushed_to_minus_infinity_gives_depth_attention,
@@ -65,6 +76,12 @@ def run_pins():
     calls.append(("library_causal_G2", pins.test_no_depth_equals_library_causal_attention, (2,)))
     calls.append(("library_autograd_G2", pins.test_backward_no_depth_equals_library_autograd,
                   (2,)))
+    calls.append(("library_noncausal_G4", pins.test_noncausal_no_depth_equals_library_attention,
+                  (4,)))
+    calls.append(("window_truncated_W3", pins.test_window_equals_operator_on_truncated_depth_cache,
+                  (True, 3)))
+    calls.append(("sparse_dO_noncausal",
+                  pins.test_sparse_upstream_gradient_token_set_backward_is_complete, (False,)))
     for name, f, args in calls:
         try:
             f(*args)
