@@ -64,6 +64,11 @@ typedef enum {
 /* Largest number of depth entries per token this build accepts. */
 #define MODA_MAX_L 1024
 
+/* moda_problem_t.flags bits. */
+#define MODA_NONCAUSAL 1 /* every sequence key 0..T-1 is visible to every query; the depth
+                            matching mask is unchanged (the MoDA README lists a non-causal
+                            kernel as future work; this is the plain reading) */
+
 typedef struct {
     int64_t B;      /* batch, >= 1 */
     int64_t Hq;     /* query heads, >= 1, multiple of Hk */
@@ -76,6 +81,13 @@ typedef struct {
     int32_t chunk;  /* tokens per query chunk requested; 0 = library default.
                        A tiling hint only: results do not depend on it beyond
                        fp32 summation order. */
+    int32_t flags;  /* 0 or MODA_NONCAUSAL */
+    int32_t window; /* depth slots visible per token: the last `window` of its L
+                       slots (rows t*L + L-window .. t*L + L-1), slots being in layer
+                       order so these are the most recent layers; 0 means all L.
+                       0 <= window <= L.  The bounded, sliding-window depth slots of
+                       the paper summary's section 6 ("Limitations and Trade-offs",
+                       mitigation status). */
     int32_t reserved; /* must be 0 */
 } moda_problem_t;
 
@@ -87,7 +99,8 @@ typedef struct {
  * Returns MODA_ERR_INVALID_ARGUMENT for: a NULL problem or pointer (other than
  * Kd/Vd with L == 0), a pointer not 16-byte aligned, B, Hq, Hk or T < 1,
  * Hq % Hk != 0, L < 0, a scale that is not finite or not > 0, reserved != 0,
- * chunk < 0, or element counts that overflow int64.  Returns
+ * chunk < 0, unknown flag bits, window < 0 or window > L, or element counts
+ * that overflow int64.  Returns
  * MODA_ERR_UNSUPPORTED for d not in {64, 128}, an unknown dtype, L > MODA_MAX_L,
  * a GQA group size G that does not divide 32, T > 2^24, T*max(L, 1) >= 2^31,
  * B*Hq >= 2^31/64, or ((G-1)*T + 64)*d*2 >= 2^31 (the 32-bit byte offsets with
@@ -147,8 +160,9 @@ int32_t moda_fwd_chunk_tokens(const moda_problem_t* p);
  * While armed, every kernel a libmoda entry point launches on this thread is
  * bracketed by two of these events, recorded on the call's stream
  * (events[2i] before and events[2i+1] after the i-th kernel since arming), as
- * long as events remain; further kernels are not timed.  The events stay owned
- * by the caller, who synchronises and reads them (hipEventElapsedTime).
+ * long as events remain and at most 4096 kernels per arming; further kernels
+ * are not timed.  The events stay owned by the caller, who synchronises and
+ * reads them (hipEventElapsedTime).
  * moda_timing_arm(NULL, 0) disarms.  Returns MODA_ERR_INVALID_ARGUMENT for a
  * negative count or NULL events with count > 0.
  */

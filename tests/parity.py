@@ -22,31 +22,39 @@ def errors(got, ref):
     return mx, rel
 
 
-# Edge shapes outside the five workloads can have outputs far larger than 1
-# (a KV-head gradient sums over up to 32 query heads).  The bf16 path rounds
-# every weight to bfloat16 before its MFMA and the output once more, so its
-# error grows with the scale of the result: for those shapes the element bound
-# is (2e-2 + 2^-8 |ref|) * max(1, rms(ref)) -- the stated absolute bound at
-# unit scale, plus one bf16 ulp of the reference, scaled by the tensor's
-# typical magnitude.  The relative Frobenius bound is unchanged.
-EDGE_REL_ELEM = {"bf16": 2.0 ** -8, "f32": 0.0}
+# Edge shapes outside the five workloads can have bf16 outputs far larger than 1
+# (a KV-head gradient sums over up to 32 query heads).  A bf16 output is rounded
+# once to bfloat16, round-to-nearest-even, and that rounding alone moves it by up
+# to 2^-8 |x| (the unit roundoff of an 8-bit significand): more than the absolute
+# 2e-2 once |x| > 5.12.  So for edge shapes the element bound of a bf16-stored
+# output is 2e-2 + 2^-8 |ref|; fp32 outputs (the log-sum-exp, and everything of the
+# fp32 path) keep the plain 2e-2.  The relative Frobenius bound is never widened.
+# The five workloads use the plain bound for every output.
+BF16_ROUNDING = 2.0 ** -8
+
+# Every check appends (name, fraction of the element bound used, fraction of the
+# relative bound used); tests/conftest.py writes them out when MODA_PARITY_REPORT
+# names a file.
+MARGINS = []
 
 
-def check(name, got, ref, dtype, report=None, edge=False):
+def check(name, got, ref, dtype, report=None, edge=False, fp32_output=False):
+    """Assert the parity bar for one output tensor.  edge: allow the bf16 output
+    rounding term (bf16-stored outputs only); fp32_output: the tensor is stored in
+    fp32 (lse), so no rounding term applies."""
     mx_tol, rel_tol = TOL[dtype]
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
     mx, rel = errors(got, ref)
-    if edge:
-        ref = np.asarray(ref, np.float64)
-        rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
-        bound = (mx_tol + EDGE_REL_ELEM[dtype] * np.abs(ref)) * max(1.0, rms)
-        excess = float((np.abs(np.asarray(got, np.float64) - ref) - bound).max())
-        ok = np.isfinite(mx) and excess <= 0 and rel <= rel_tol
-        line = (f"{name}: max_abs={mx:.3e} (<= ({mx_tol:g} + 2^-8|ref|) x {max(1.0, rms):.2f}, "
-                f"worst excess {excess:.2e}) rel_fro={rel:.3e} (<= {rel_tol:g})")
-    else:
-        ok = np.isfinite(mx) and mx <= mx_tol and rel <= rel_tol
-        line = f"{name}: max_abs={mx:.3e} (<= {mx_tol:g}) rel_fro={rel:.3e} (<= {rel_tol:g})"
+    rounding = BF16_ROUNDING if (edge and dtype == "bf16" and not fp32_output) else 0.0
+    bound = mx_tol + rounding * np.abs(ref)
+    used = float((np.abs(got - ref) / bound).max()) if ref.size else 0.0
+    ok = np.isfinite(mx) and used <= 1.0 and rel <= rel_tol
+    term = f"{mx_tol:g} + 2^-8|ref|" if rounding else f"{mx_tol:g}"
+    line = (f"{name}: max_abs={mx:.3e} (<= {term}; {100 * used:.1f}% of the element bound) "
+            f"rel_fro={rel:.3e} (<= {rel_tol:g}; {100 * rel / rel_tol:.1f}%)")
     print(line, flush=True)
+    MARGINS.append((name, used, rel / rel_tol))
     if report is not None:
         report.append(line)
     assert ok, line

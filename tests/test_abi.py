@@ -54,6 +54,7 @@ INVALID_PROBLEMS = [
     dict(B=0), dict(Hq=0), dict(Hk=0), dict(T=0), dict(T=-3), dict(Hq=5, Hk=2), dict(L=-1),
     dict(scale=0.0), dict(scale=-1.0), dict(scale=float("inf")), dict(scale=float("nan")),
     dict(chunk=-1), dict(reserved=1), dict(B=1 << 40, T=1 << 30, Hq=1 << 20, Hk=1 << 20),
+    dict(flags=2), dict(flags=-1), dict(window=-1), dict(window=3), dict(L=0, window=1),
 ]
 UNSUPPORTED_PROBLEMS = [
     dict(d=32), dict(d=96), dict(d=256), dict(dtype=7), dict(L=mb.MODA_MAX_L + 1),

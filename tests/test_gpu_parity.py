@@ -1,10 +1,15 @@
 """GPU parity: libmoda (through the C ABI) against the CPU oracle, element by
 element, on the same seeded inputs.
 
-Small and medium workloads are compared in full; the 64K-token workload on
-sampled query rows (forward rows are independent, so each sampled row is
-exact) and on gradients the oracle computes exactly from a subset of rows;
-invariants of the definition cover the rest at full size."""
+Small and medium workloads are compared in full.  The 64K-token workload, at
+the size and launch configuration the benchmark times, is compared on sampled
+forward rows (rows are independent, so each is exact); on exact oracle
+gradients of token ranges (dQ and the depth gradients of those tokens, and
+every dK, dV row of the last 4096 keys); on every dK and dV row of every KV
+group under an upstream gradient that is zero outside a token set (rows with
+zero upstream gradient contribute nothing, so the oracle's restricted backward
+is then complete, while the kernels still walk every query tile); and on three
+full-size gradient invariants of the definition per KV group."""
 import numpy as np
 import pytest
 import torch
@@ -24,7 +29,7 @@ def fwd_full_check(w, x, chunk=0, label="", edge=False):
     h = oracle_inputs(x)
     Or, lr = oracle.fwd(h["Q"], h["K"], h["V"], h.get("Kd"), h.get("Vd"), w.L, w.scale)
     check(f"{w.name}{label} O", to64(O), Or, w.dtype, edge=edge)
-    check(f"{w.name}{label} lse", to64(lse), lr, w.dtype, edge=edge)
+    check(f"{w.name}{label} lse", to64(lse), lr, w.dtype, edge=edge, fp32_output=True)
     return O, lse
 
 
@@ -68,7 +73,7 @@ def test_layer_1p5b_forward_one_kv_group_and_no_depth_path():
         Or, lr = oracle.fwd_rows(h["Q"], h["K"], h["V"], h["Kd"], h["Vd"], L, w.scale, rows)
         check(f"{w.name} L={L} O (kv group {kv})", gather_rows(O, rows), Or, w.dtype)
         check(f"{w.name} L={L} lse (kv group {kv})", gather_rows(lse, rows)[:, None],
-              lr[:, None], w.dtype)
+              lr[:, None], w.dtype, fp32_output=True)
 
 
 def long_rows(w):
@@ -92,22 +97,65 @@ def test_long_64k_forward_sampled_rows():
     Or, lr = oracle.fwd_rows(h["Q"], h["K"], h["V"], h["Kd"], h["Vd"], w.L, w.scale, rows)
     check(f"{w.name} O ({len(rows)} sampled rows)", gather_rows(O, rows), Or, w.dtype)
     check(f"{w.name} lse ({len(rows)} sampled rows)", gather_rows(lse, rows)[:, None],
-          lr[:, None], w.dtype)
+          lr[:, None], w.dtype, fp32_output=True)
 
 
-def test_long_64k_backward_sampled_token_ranges():
-    """The timed step's backward at its full size and launch configuration, against exact
-    oracle gradients of three token ranges.  For KV group (b, kv) and tokens [t_lo, t_hi)
-    the oracle's dQ rows and the depth rows' dKd, dVd are complete; with t_hi = T the dK
-    and dV rows at or after t_lo are complete too (only those tokens' queries see them)."""
+@pytest.fixture(scope="module")
+def long64k():
+    """The 64K workload's inputs (seed 6), its forward, and exact host copies."""
     w = W["long_64k"]
     x = inputs.make(w, seed=6, device=DEV, names=("Q", "K", "V", "Kd", "Vd", "dO"))
     O, lse = run_fwd(x, w)
+    torch.cuda.synchronize()
+    yield w, x, O, lse, oracle_inputs(x)
+    del x, O, lse
+    torch.cuda.empty_cache()
+
+
+def invariant_residuals(w, x, grads, b, kv):
+    """The three gradient identities of the definition for KV group (b, kv), in fp64 on the
+    device: (sum dK + sum dKd, sum dV + sum dVd - sum dO, <Q,dQ> - <K,dK> - <Kd,dKd>), each
+    with the scale of the terms that make it up (the root sum of squares of the summed
+    elements, or of the elementwise products)."""
+    dQ, dK, dV, dKd, dVd = grads
+    G = w.G
+    hs = slice(kv * G, (kv + 1) * G)
+    f = lambda t: t.double()  # noqa: E731
+    sk = f(dK[b, kv]).sum(0) + f(dKd[b, kv]).sum(0)
+    nk = (f(dK[b, kv]).square().sum(0) + f(dKd[b, kv]).square().sum(0)).sqrt()
+    sv = f(dV[b, kv]).sum(0) + f(dVd[b, kv]).sum(0) - f(x["dO"][b, hs]).sum((0, 1))
+    nv = (f(dV[b, kv]).square().sum(0) + f(dVd[b, kv]).square().sum(0)).sqrt()
+    pq = f(x["Q"][b, hs]) * f(dQ[b, hs])
+    pk = f(x["K"][b, kv]) * f(dK[b, kv])
+    pd = f(x["Kd"][b, kv]) * f(dKd[b, kv])
+    sp = pq.sum() - pk.sum() - pd.sum()
+    npp = (pq.square().sum() + pk.square().sum() + pd.square().sum()).sqrt()
+    return [(n, r.cpu().numpy(), s.cpu().numpy()) for n, r, s in
+            (("sum dK + sum dKd", sk, nk), ("sum dV + sum dVd - sum dO", sv, nv),
+             ("<Q,dQ> - <K,dK> - <Kd,dKd>", sp, npp))]
+
+
+def test_long_64k_backward_exact_ranges_and_invariants(long64k):
+    """The timed step's backward at its full size and launch configuration.
+    Exact oracle gradients: for KV group (b, kv) and tokens [t_lo, t_hi) the oracle's dQ
+    rows and the depth rows' dKd, dVd are complete; with t_hi = T the dK and dV rows at or
+    after t_lo are complete too (only those tokens' queries see them): the last 4096 keys.
+    Full size, every KV group: the identities of the definition
+      sum_j dK_j + sum_r dKd_r = 0        (shifting every key by one vector shifts each
+                                           row's scores by a constant),
+      sum_j dV_j + sum_r dVd_r = sum dO   (adding one vector to every value adds it to
+                                           every output),
+      <Q,dQ> = <K,dK> + <Kd,dKd>          (scaling queries by c and keys by 1/c changes
+                                           no score).
+    Tolerance: if every element's error is independent with an RMS within the parity bar's
+    relative Frobenius bound eps = 1e-2 of the values' RMS, a sum's error has standard
+    deviation at most eps times the root sum of squares of its terms; six such deviations
+    are allowed."""
+    w, x, O, lse, h = long64k
     dQ, dK, dV, dKd, dVd = run_bwd(x, w, O, lse)
     torch.cuda.synchronize()
-    h = oracle_inputs(x)
     G, T, L = w.G, w.T, w.L
-    for b, kv, t_lo, t_hi in ((0, 0, T - 40, T), (0, 5, 30000, 30024), (0, 7, 0, 24)):
+    for b, kv, t_lo, t_hi in ((0, 0, T - 4096, T), (0, 5, 30000, 30024), (0, 7, 0, 24)):
         g = oracle.bwd_group(h["Q"], h["K"], h["V"], h["Kd"], h["Vd"], h["dO"], L, w.scale,
                              b, kv, t_lo, t_hi)
         hs, ts = slice(kv * G, (kv + 1) * G), slice(t_lo, t_hi)
@@ -118,6 +166,57 @@ def test_long_64k_backward_sampled_token_ranges():
         if t_hi == T:
             check(f"{tag} dK", to64(dK[b, kv, t_lo:]), g["dK"][t_lo:], w.dtype)
             check(f"{tag} dV", to64(dV[b, kv, t_lo:]), g["dV"][t_lo:], w.dtype)
+    eps = 1e-2
+    for kv in range(w.Hk):
+        for name, r, scale in invariant_residuals(w, x, (dQ, dK, dV, dKd, dVd), 0, kv):
+            tol = 6 * eps * scale
+            used = float(np.max(np.abs(r) / tol))
+            print(f"{w.name} kv={kv} {name}: max |residual| {np.max(np.abs(r)):.3e}, "
+                  f"{100 * used:.1f}% of the tolerance", flush=True)
+            assert used <= 1.0, (kv, name)
+
+
+def sparse_tokens(T):
+    """Tokens of the sparse upstream gradient: both ends, spread points and query-tile
+    boundaries, so that every key block's walk meets nonzero rows early and late."""
+    tok = set(range(8)) | set(range(T - 8, T)) | set(np.linspace(0, T - 1, 64).astype(int))
+    for c in (1, 255, 256, 300, 511):
+        tok |= {c * 128 - 1, c * 128}
+    return np.array(sorted(t for t in tok if 0 <= t < T))
+
+
+def test_long_64k_backward_every_key_gradient_under_sparse_upstream(long64k):
+    """dO zero outside a token set S: rows outside S contribute exactly nothing to any
+    gradient (dS = p (dO.v - D) and p dO vanish; D = <dO, O> = 0), on the GPU as in exact
+    arithmetic.  The kernels still walk every query tile, so every dK and dV row of every KV
+    group -- including the key blocks that walk all 131072 folded query rows -- is compared
+    with the oracle's complete restricted backward, along with dQ and the depth gradients of
+    S (the depth rows of other tokens must be exactly zero)."""
+    w, x, O, lse, h = long64k
+    G, T, L = w.G, w.T, w.L
+    S = sparse_tokens(T)
+    dO = torch.zeros_like(x["dO"])
+    idx = torch.from_numpy(S).to(DEV)
+    dO[:, :, idx] = x["dO"][:, :, idx]
+    xs = dict(x, dO=dO)
+    dQ, dK, dV, dKd, dVd = run_bwd(xs, w, O, lse)
+    torch.cuda.synchronize()
+    hdO = host(dO)
+    rows = (torch.from_numpy(S)[:, None] * L + torch.arange(L)[None, :]).reshape(-1).to(DEV)
+    other = torch.ones(T * L, dtype=torch.bool, device=DEV)
+    other[rows] = False
+    for kv in range(w.Hk):
+        g = oracle.bwd_tokens(h["Q"], h["K"], h["V"], h["Kd"], h["Vd"], hdO, L, w.scale, 0, kv,
+                              S)
+        hs = slice(kv * G, (kv + 1) * G)
+        tag = f"{w.name} sparse dO ({len(S)} tokens) kv={kv}"
+        check(f"{tag} dK (all {T} keys)", to64(dK[0, kv]), g["dK"], w.dtype)
+        check(f"{tag} dV (all {T} keys)", to64(dV[0, kv]), g["dV"], w.dtype)
+        check(f"{tag} dQ", to64(dQ[0, hs][:, idx]), g["dQ"], w.dtype)
+        check(f"{tag} dKd", to64(dKd[0, kv, rows]), g["dKd"], w.dtype)
+        check(f"{tag} dVd", to64(dVd[0, kv, rows]), g["dVd"], w.dtype)
+        assert not torch.any(dKd[0, kv, other] != 0) and not torch.any(dVd[0, kv, other] != 0)
+        assert not torch.any(dQ[0, hs][:, ~torch.isin(torch.arange(T, device=DEV), idx)] != 0)
 
 
 def test_million_token_sequence_sampled():
@@ -137,7 +236,7 @@ def test_million_token_sequence_sampled():
     Or, lr = oracle.fwd_rows(h["Q"], h["K"], h["V"], h["Kd"], h["Vd"], L, w.scale, rows)
     check(f"{w.name} O ({len(rows)} sampled rows)", gather_rows(O, rows), Or, w.dtype)
     check(f"{w.name} lse ({len(rows)} sampled rows)", gather_rows(lse, rows)[:, None],
-          lr[:, None], w.dtype)
+          lr[:, None], w.dtype, fp32_output=True)
     g = oracle.bwd_group(h["Q"], h["K"], h["V"], h["Kd"], h["Vd"], h["dO"], L, w.scale, 0, 0,
                          T - n, T)
     tag = f"{w.name} (tokens {T - n}..{T - 1})"
@@ -162,7 +261,7 @@ def test_train_4k_forward_backward_two_kv_groups():
         hs = slice(kv * G, (kv + 1) * G)
         tag = f"{w.name} (b={b}, kv={kv})"
         check(f"{tag} O", to64(O[b, hs]), g["O"], w.dtype)
-        check(f"{tag} lse", to64(lse[b, hs]), g["lse"], w.dtype)
+        check(f"{tag} lse", to64(lse[b, hs]), g["lse"], w.dtype, fp32_output=True)
         check(f"{tag} dQ", to64(dQ[b, hs]), g["dQ"], w.dtype)
         check(f"{tag} dK", to64(dK[b, kv]), g["dK"], w.dtype)
         check(f"{tag} dV", to64(dV[b, kv]), g["dV"], w.dtype)

@@ -1,11 +1,14 @@
 """ctypes binding of libmoda (include/moda.h): argument marshalling only.
 
 The functions named like the C entry points (``moda_fwd``, ``moda_bwd``, ...)
-take torch tensors that the caller allocated, pass their device pointers and
-the current HIP stream, and raise ``ModaError`` on a non-OK status.  ``fwd``,
-``bwd`` and ``pack_depth`` additionally allocate the outputs with torch.  Every
-step of the computation runs in the HIP kernels of libmoda.so; there is no
-fallback: if the library is missing this module raises.
+take torch tensors that the caller allocated, check that each one is a
+contiguous GPU tensor of the shape and dtype the problem implies (the C ABI
+takes bare pointers and cannot), pass their device pointers and the current
+HIP stream, and raise ``ModaError`` on a non-OK status.  A plain int is taken
+as a raw device pointer and passed through unchecked.  ``fwd``, ``bwd`` and
+``pack_depth`` additionally allocate the outputs with torch.  Every step of the
+computation runs in the HIP kernels of libmoda.so; there is no fallback: if the
+library is missing this module raises.
 """
 from __future__ import annotations
 
@@ -20,6 +23,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoda.so"
 MODA_OK, MODA_ERR_INVALID_ARGUMENT, MODA_ERR_UNSUPPORTED, MODA_ERR_HIP = 0, 1, 2, 3
 MODA_BF16, MODA_F32 = 0, 1
 MODA_MAX_L = 1024
+MODA_NONCAUSAL = 1
+_TORCH_DTYPE = {MODA_BF16: torch.bfloat16, MODA_F32: torch.float32}
 
 EXPORTS = ("moda_fwd", "moda_bwd", "moda_bwd_workspace_bytes", "moda_pack_depth",
            "moda_status_string", "moda_last_error", "moda_fwd_chunk_tokens", "moda_timing_arm",
@@ -36,7 +41,7 @@ class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hk", ctypes.c_int64),
                 ("T", ctypes.c_int64), ("d", ctypes.c_int64), ("L", ctypes.c_int64),
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("chunk", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("flags", ctypes.c_int32), ("window", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -75,18 +80,65 @@ def load(path: str = LIB_PATH):
     return _lib
 
 
-def problem(B, Hq, Hk, T, d, L, scale=None, dtype=MODA_BF16, chunk=0, reserved=0) -> Problem:
+def problem(B, Hq, Hk, T, d, L, scale=None, dtype=MODA_BF16, chunk=0, flags=0, window=0,
+            reserved=0) -> Problem:
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    return Problem(B, Hq, Hk, T, d, L, scale, dtype, chunk, reserved)
+    return Problem(B, Hq, Hk, T, d, L, scale, dtype, chunk, flags, window, reserved)
 
 
-def problem_for(Q: torch.Tensor, K: torch.Tensor, L: int, scale=None, chunk=0) -> Problem:
+def problem_for(Q: torch.Tensor, K: torch.Tensor, L: int, scale=None, chunk=0, causal=True,
+                window=0) -> Problem:
+    if Q.dim() != 4 or K.dim() != 4:
+        raise ValueError(f"Q and K must be 4-D [B,H,T,d]; got {tuple(Q.shape)}, {tuple(K.shape)}")
     B, Hq, T, d = Q.shape
     dt = {torch.bfloat16: MODA_BF16, torch.float32: MODA_F32}.get(Q.dtype)
     if dt is None:
         raise TypeError(f"unsupported dtype {Q.dtype}")
-    return problem(B, Hq, K.shape[1], T, d, L, scale, dt, chunk)
+    return problem(B, Hq, K.shape[1], T, d, L, scale, dt, chunk,
+                   0 if causal else MODA_NONCAUSAL, window)
+
+
+def _structure(name, t, shape, dtype, optional=False):
+    """Raise unless t is a contiguous tensor of this shape and dtype.  An int is a raw
+    device pointer, passed unchecked; None is allowed only when optional."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if isinstance(t, int):
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor or a raw device pointer")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}; the problem needs {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}; the problem needs {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} is not contiguous (a transposed or strided view?)")
+
+
+def _check_tensors(specs):
+    """specs: (name, tensor, shape, dtype[, optional]).  First every tensor's shape,
+    dtype and layout, then that all of them sit on one GPU."""
+    for spec in specs:
+        _structure(*spec)
+    dev = None
+    for name, t, *_ in specs:
+        if not isinstance(t, torch.Tensor):
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} is on {t.device}, not on a GPU")
+        if dev is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}; the other tensors are on {dev}")
+        dev = t.device
+
+
+def _shapes(p: Problem):
+    q = (p.B, p.Hq, p.T, p.d)
+    kv = (p.B, p.Hk, p.T, p.d)
+    dep = (p.B, p.Hk, p.T * p.L, p.d)
+    return q, kv, dep, (p.B, p.Hq, p.T)
 
 
 def _ptr(t):
@@ -111,6 +163,13 @@ def _check(rc: int):
 
 
 def moda_fwd(p: Problem, Q, K, V, Kd, Vd, O, lse, stream=None) -> None:
+    dt = _TORCH_DTYPE.get(p.dtype)
+    if dt is not None:
+        q, kv, dep, rows = _shapes(p)
+        nodep = p.L == 0
+        _check_tensors([("Q", Q, q, dt), ("K", K, kv, dt), ("V", V, kv, dt),
+                        ("Kd", Kd, dep, dt, nodep), ("Vd", Vd, dep, dt, nodep),
+                        ("O", O, q, dt), ("lse", lse, rows, torch.float32)])
     _check(load().moda_fwd(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Kd), _ptr(Vd),
                            _ptr(O), _ptr(lse), _stream(stream)))
 
@@ -121,8 +180,23 @@ def moda_bwd_workspace_bytes(p: Problem) -> int:
 
 def moda_bwd(p: Problem, Q, K, V, Kd, Vd, O, lse, dO, dQ, dK, dV, dKd, dVd, workspace,
              workspace_bytes=None, stream=None) -> None:
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size()
+    dt = _TORCH_DTYPE.get(p.dtype)
+    if dt is not None:
+        q, kv, dep, rows = _shapes(p)
+        nodep = p.L == 0
+        _check_tensors([("Q", Q, q, dt), ("K", K, kv, dt), ("V", V, kv, dt),
+                        ("Kd", Kd, dep, dt, nodep), ("Vd", Vd, dep, dt, nodep),
+                        ("O", O, q, dt), ("lse", lse, rows, torch.float32), ("dO", dO, q, dt),
+                        ("dQ", dQ, q, dt), ("dK", dK, kv, dt), ("dV", dV, kv, dt),
+                        ("dKd", dKd, dep, dt, nodep), ("dVd", dVd, dep, dt, nodep)])
+    if isinstance(workspace, torch.Tensor):
+        if not workspace.is_contiguous() or workspace.device.type != "cuda":
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        nbytes = workspace.numel() * workspace.element_size()
+        if workspace_bytes is None or workspace_bytes > nbytes:
+            workspace_bytes = nbytes
+    elif workspace_bytes is None:
+        raise ValueError("workspace_bytes is required with a raw workspace pointer")
     _check(load().moda_bwd(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Kd), _ptr(Vd),
                            _ptr(O), _ptr(lse), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV),
                            _ptr(dKd), _ptr(dVd), _ptr(workspace), int(workspace_bytes),
@@ -130,6 +204,10 @@ def moda_bwd(p: Problem, Q, K, V, Kd, Vd, O, lse, dO, dQ, dK, dV, dKd, dVd, work
 
 
 def moda_pack_depth(p: Problem, layers, packed, stream=None) -> None:
+    dt = _TORCH_DTYPE.get(p.dtype)
+    if dt is not None:
+        _check_tensors([("layers", layers, (p.L, p.B, p.Hk, p.T, p.d), dt),
+                        ("packed", packed, (p.B, p.Hk, p.T * p.L, p.d), dt)])
     _check(load().moda_pack_depth(ctypes.byref(p), _ptr(layers), _ptr(packed), _stream(stream)))
 
 
@@ -175,7 +253,8 @@ class KernelTimer:
             ms = ctypes.c_float()
             if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
                 raise RuntimeError("hipEventElapsedTime failed")
-            out.append((lib.moda_timing_label(i).decode(), ms.value))
+            label = lib.moda_timing_label(i)
+            out.append((label.decode() if label else "?", ms.value))
         return out
 
     def close(self):
@@ -187,18 +266,19 @@ class KernelTimer:
 
 # ---- allocating conveniences (torch allocates; libmoda computes) ----
 
-def fwd(Q, K, V, Kd, Vd, L, scale=None, chunk=0, stream=None):
+def fwd(Q, K, V, Kd, Vd, L, scale=None, chunk=0, stream=None, causal=True, window=0):
     """O [B,Hq,T,d] (dtype of Q) and lse [B,Hq,T] fp32."""
-    p = problem_for(Q, K, L, scale, chunk)
+    p = problem_for(Q, K, L, scale, chunk, causal, window)
     O = torch.empty_like(Q)
     lse = torch.empty(Q.shape[:3], device=Q.device, dtype=torch.float32)
     moda_fwd(p, Q, K, V, Kd, Vd, O, lse, stream)
     return O, lse
 
 
-def bwd(Q, K, V, Kd, Vd, O, lse, dO, L, scale=None, chunk=0, stream=None):
+def bwd(Q, K, V, Kd, Vd, O, lse, dO, L, scale=None, chunk=0, stream=None, causal=True,
+        window=0):
     """(dQ, dK, dV, dKd, dVd); dKd/dVd are None when L == 0."""
-    p = problem_for(Q, K, L, scale, chunk)
+    p = problem_for(Q, K, L, scale, chunk, causal, window)
     dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
     dKd = torch.empty_like(Kd) if L > 0 else None
     dVd = torch.empty_like(Vd) if L > 0 else None
@@ -209,8 +289,12 @@ def bwd(Q, K, V, Kd, Vd, O, lse, dO, L, scale=None, chunk=0, stream=None):
 
 def pack_depth(layers, stream=None):
     """layers [L,B,Hk,T,d] -> packed [B,Hk,T*L,d]."""
+    if layers.dim() != 5:
+        raise ValueError(f"layers must be [L,B,Hk,T,d]; got shape {tuple(layers.shape)}")
     L, B, Hk, T, d = layers.shape
-    dt = {torch.bfloat16: MODA_BF16, torch.float32: MODA_F32}[layers.dtype]
+    dt = {torch.bfloat16: MODA_BF16, torch.float32: MODA_F32}.get(layers.dtype)
+    if dt is None:
+        raise TypeError(f"unsupported dtype {layers.dtype}")
     p = problem(B, Hk, Hk, T, d, L, 1.0, dt)
     out = torch.empty((B, Hk, T * L, d), device=layers.device, dtype=layers.dtype)
     moda_pack_depth(p, layers, out, stream)

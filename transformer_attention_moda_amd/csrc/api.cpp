@@ -58,6 +58,11 @@ moda_status_t check_problem(const moda_problem_t* p, bool need_head_dim, moda::S
         return fail(MODA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
     if (p->reserved != 0) return fail(MODA_ERR_INVALID_ARGUMENT, "reserved field must be 0");
     if (p->chunk < 0) return fail(MODA_ERR_INVALID_ARGUMENT, "chunk must be >= 0");
+    if (p->flags & ~MODA_NONCAUSAL)
+        return fail(MODA_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", (unsigned)p->flags);
+    if (p->window < 0 || p->window > p->L)
+        return fail(MODA_ERR_INVALID_ARGUMENT, "window %d outside 0..L (L = %lld)", (int)p->window,
+                    (long long)p->L);
     if (p->dtype != MODA_BF16 && p->dtype != MODA_F32)
         return fail(MODA_ERR_UNSUPPORTED, "unknown dtype %d", (int)p->dtype);
     int64_t n = 0;
@@ -83,6 +88,8 @@ moda_status_t check_problem(const moda_problem_t* p, bool need_head_dim, moda::S
         return fail(MODA_ERR_UNSUPPORTED,
                     "(G-1)*T = %lld rows of d = %lld exceed the 2 GiB reach of the staging offsets",
                     (long long)((G - 1) * p->T), (long long)p->d);
+    if (p->flags != 0 || (p->window != 0 && p->window != p->L))
+        return fail(MODA_ERR_UNSUPPORTED, "non-causal or windowed depth not built yet");
     if (s) {
         s->B = p->B; s->Hq = p->Hq; s->Hk = p->Hk; s->T = p->T; s->d = p->d; s->L = p->L;
         s->scale = p->scale;
@@ -134,11 +141,13 @@ size_t bwd_ws_bytes(const moda::Shape& s, int32_t dtype)
     return (n + 255) & ~size_t(255);
 }
 
+constexpr int32_t kMaxTimedKernels = 4096;
+
 struct Timing {
     hipEvent_t* events = nullptr;
     int32_t count = 0;
     int32_t used = 0;   // events recorded
-    const char* labels[512];
+    const char* labels[kMaxTimedKernels];
     int32_t nlabels = 0;
 };
 thread_local Timing g_timing;
@@ -150,9 +159,11 @@ namespace moda {
 void timing_begin(const char* label, hipStream_t st)
 {
     Timing& t = g_timing;
-    if (!t.events || t.used + 2 > t.count) return;
+    // A kernel is timed only while both of its events and a label slot remain, so that
+    // every bracketed kernel has a label.
+    if (!t.events || t.used + 2 > t.count || t.nlabels >= kMaxTimedKernels) return;
     (void)hipEventRecord(t.events[t.used++], st);
-    if (t.nlabels < 512) t.labels[t.nlabels++] = label;
+    t.labels[t.nlabels++] = label;
 }
 
 void timing_end(hipStream_t st)
@@ -181,7 +192,7 @@ int32_t moda_timing_count(void) { return g_timing.used / 2; }
 
 const char* moda_timing_label(int32_t i)
 {
-    if (i < 0 || i >= g_timing.nlabels || i >= g_timing.used / 2) return nullptr;
+    if (i < 0 || i >= g_timing.used / 2) return nullptr;
     return g_timing.labels[i];
 }
 
