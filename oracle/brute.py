@@ -105,3 +105,39 @@ def backward(Q, K, V, Kd, Vd, dO, L, scale, causal=True, window=0):
             if L > 0:
                 dKd[b, kv], dVd[b, kv] = dkeys[T:], dvals[T:]
     return dQ, dK, dV, dKd, dVd
+
+
+def abs_terms(Q, K, V, Kd, Vd, dO, L, scale, causal=True, window=0):
+    """Per output element, the sum of the absolute values of the terms of the product that
+    yields it (exact fp64 weights): O = P V -> P |V|; dV, dVd = P^T dO -> P^T |dO|;
+    dQ = scale dS [K||Kd] -> scale |dS| [|K|||Kd|]; dK, dKd = scale dS^T Q -> scale
+    |dS|^T |Q|.  A product whose left operand is rounded to a format of unit roundoff u
+    before an exactly accumulated sum is off by at most u times this (first order), which
+    sizes the tolerance of outputs that are sums of many such terms.  Dict keyed like the
+    outputs (dO may be None: forward only)."""
+    B, Hq, T, d = Q.shape
+    Hk = K.shape[1]
+    G = Hq // Hk
+    out = {"O": np.zeros((B, Hq, T, d))}
+    if dO is not None:
+        out.update(dQ=np.zeros_like(Q), dK=np.zeros_like(K), dV=np.zeros_like(V),
+                   dKd=np.zeros((B, Hk, T * L, d)), dVd=np.zeros((B, Hk, T * L, d)))
+    for b in range(B):
+        for kv in range(Hk):
+            Qf, keys, vals, M, G, T = _group(Q, K, V, Kd, Vd, L, b, kv, causal, window)
+            S = (Qf @ keys.T) * scale + M
+            E = np.exp(S - S.max(axis=1, keepdims=True))
+            P = E / E.sum(axis=1, keepdims=True)
+            out["O"][b, kv * G:(kv + 1) * G] = _unfold(P @ np.abs(vals), G, T)
+            if dO is None:
+                continue
+            dOf = np.transpose(dO[b, kv * G:(kv + 1) * G], (1, 0, 2)).reshape(T * G, d)
+            Of = P @ vals
+            dS = np.abs(P * (dOf @ vals.T - (dOf * Of).sum(axis=1, keepdims=True)))
+            out["dQ"][b, kv * G:(kv + 1) * G] = _unfold(scale * dS @ np.abs(keys), G, T)
+            dk = scale * dS.T @ np.abs(Qf)
+            dv = P.T @ np.abs(dOf)
+            out["dK"][b, kv], out["dV"][b, kv] = dk[:T], dv[:T]
+            if L > 0:
+                out["dKd"][b, kv], out["dVd"][b, kv] = dk[T:], dv[T:]
+    return out

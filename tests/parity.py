@@ -22,14 +22,18 @@ def errors(got, ref):
     return mx, rel
 
 
-# Edge shapes outside the five workloads can have bf16 outputs far larger than 1
-# (a KV-head gradient sums over up to 32 query heads).  A bf16 output is rounded
-# once to bfloat16, round-to-nearest-even, and that rounding alone moves it by up
-# to 2^-8 |x| (the unit roundoff of an 8-bit significand): more than the absolute
-# 2e-2 once |x| > 5.12.  So for edge shapes the element bound of a bf16-stored
-# output is 2e-2 + 2^-8 |ref|; fp32 outputs (the log-sum-exp, and everything of the
-# fp32 path) keep the plain 2e-2.  The relative Frobenius bound is never widened.
-# The five workloads use the plain bound for every output.
+# Edge shapes outside the five workloads (up to 32 query heads per KV head, up to
+# 1024 depth slots) have bf16 outputs that are large, or small sums of many large
+# terms.  The bf16 path rounds each weight P (and each dS) to bfloat16 before its
+# MFMA, and rounds every output once more (round-to-nearest-even, unit roundoff
+# u = 2^-8 for an 8-bit significand).  To first order, a sum of terms a_i b_i whose
+# a_i are so rounded is off by at most u * sum |a_i b_i|, and the output rounding by
+# u |x|.  So for edge shapes the element bound of a bf16-stored output is
+#   2e-2 + 2^-8 (|ref| + A),
+# A being the sum of the absolute values of that output's terms (oracle.brute.abs_terms);
+# fp32 outputs (the log-sum-exp, and everything of the fp32 path) keep the plain 2e-2.
+# The relative Frobenius bound is never widened.  The five workloads use the plain
+# bound for every output.
 BF16_ROUNDING = 2.0 ** -8
 
 # Every check appends (name, fraction of the element bound used, fraction of the
@@ -38,19 +42,20 @@ BF16_ROUNDING = 2.0 ** -8
 MARGINS = []
 
 
-def check(name, got, ref, dtype, report=None, edge=False, fp32_output=False):
-    """Assert the parity bar for one output tensor.  edge: allow the bf16 output
-    rounding term (bf16-stored outputs only); fp32_output: the tensor is stored in
-    fp32 (lse), so no rounding term applies."""
+def check(name, got, ref, dtype, report=None, edge=False, fp32_output=False, terms=None):
+    """Assert the parity bar for one output tensor.  edge: allow the bf16 rounding terms
+    (bf16-stored outputs only), with `terms` the absolute-term sums A of the output;
+    fp32_output: the tensor is stored in fp32 (lse), so no rounding term applies."""
     mx_tol, rel_tol = TOL[dtype]
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     mx, rel = errors(got, ref)
     rounding = BF16_ROUNDING if (edge and dtype == "bf16" and not fp32_output) else 0.0
-    bound = mx_tol + rounding * np.abs(ref)
+    A = 0.0 if terms is None else np.asarray(terms, np.float64)
+    bound = mx_tol + rounding * (np.abs(ref) + A)
     used = float((np.abs(got - ref) / bound).max()) if ref.size else 0.0
     ok = np.isfinite(mx) and used <= 1.0 and rel <= rel_tol
-    term = f"{mx_tol:g} + 2^-8|ref|" if rounding else f"{mx_tol:g}"
+    term = f"{mx_tol:g} + 2^-8(|ref| + A)" if rounding else f"{mx_tol:g}"
     line = (f"{name}: max_abs={mx:.3e} (<= {term}; {100 * used:.1f}% of the element bound) "
             f"rel_fro={rel:.3e} (<= {rel_tol:g}; {100 * rel / rel_tol:.1f}%)")
     print(line, flush=True)

@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import brute
 from transformer_attention_moda_amd import binding, inputs
 from parity import (check, gather_rows, host, oracle_inputs, rows_array, run_bwd, run_fwd, to64)
 
@@ -23,12 +24,20 @@ DEV = "cuda:0"
 W = inputs.WORKLOADS
 
 
+def abs_terms(w, x):
+    """Absolute-term sums of every output (oracle.brute), for the edge-shape bound."""
+    f = {k: (to64(v) if v is not None else None) for k, v in x.items()}
+    return brute.abs_terms(f["Q"], f["K"], f["V"], f.get("Kd"), f.get("Vd"), f.get("dO"), w.L,
+                           w.scale)
+
+
 def fwd_full_check(w, x, chunk=0, label="", edge=False):
     O, lse = run_fwd(x, w, chunk)
     torch.cuda.synchronize()
     h = oracle_inputs(x)
     Or, lr = oracle.fwd(h["Q"], h["K"], h["V"], h.get("Kd"), h.get("Vd"), w.L, w.scale)
-    check(f"{w.name}{label} O", to64(O), Or, w.dtype, edge=edge)
+    A = abs_terms(w, x) if edge else {}
+    check(f"{w.name}{label} O", to64(O), Or, w.dtype, edge=edge, terms=A.get("O"))
     check(f"{w.name}{label} lse", to64(lse), lr, w.dtype, edge=edge, fp32_output=True)
     return O, lse
 
@@ -41,8 +50,9 @@ def bwd_full_check(w, x, O, lse, chunk=0, label="", edge=False):
     got = {"dQ": dQ, "dK": dK, "dV": dV}
     if w.L > 0:
         got.update(dKd=dKd, dVd=dVd)
+    A = abs_terms(w, x) if edge else {}
     for k, v in got.items():
-        check(f"{w.name}{label} {k}", to64(v), g[k], w.dtype, edge=edge)
+        check(f"{w.name}{label} {k}", to64(v), g[k], w.dtype, edge=edge, terms=A.get(k))
 
 
 # ---------------- the five workloads ----------------
