@@ -131,6 +131,28 @@ moda_status_t moda_bwd(const moda_problem_t* p, const void* Q, const void* K, co
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moda_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The per-row scratch that moda_bwd keeps in the
+ * caller's workspace lives instead in a static device array of
+ * MODA_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held from the library's first
+ * use on that GPU until the process ends.  Nothing is allocated or freed.
+ * Problems whose moda_bwd_workspace_bytes exceeds that size return
+ * MODA_ERR_UNSUPPORTED (at d = 128 with depth rows: about 516K query rows
+ * B*Hq*T).  Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (different streams, or different host threads) race and
+ * give wrong results; serialise them.  `stream` must belong to the calling
+ * thread's current device.  Other arguments, results and errors as for
+ * moda_bwd, which it matches bit for bit.
+ */
+#define MODA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+moda_status_t moda_bwd_noalloc(const moda_problem_t* p, const void* Q, const void* K,
+                               const void* V, const void* Kd, const void* Vd, const void* O,
+                               const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                               void* dKd, void* dVd, void* stream);
+
+/*
  * Depth-KV layout packer: layer-major depth entries layers[L, B, Hk, T, d]
  * (entry l of every token contiguous, the natural per-layer layout whose
  * stride between a token's layers defeats coalescing) to the token-major

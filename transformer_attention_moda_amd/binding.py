@@ -24,9 +24,11 @@ MODA_OK, MODA_ERR_INVALID_ARGUMENT, MODA_ERR_UNSUPPORTED, MODA_ERR_HIP = 0, 1, 2
 MODA_BF16, MODA_F32 = 0, 1
 MODA_MAX_L = 1024
 MODA_NONCAUSAL = 1
+MODA_NOALLOC_SCRATCH_BYTES = 256 << 20
 _TORCH_DTYPE = {MODA_BF16: torch.bfloat16, MODA_F32: torch.float32}
 
-EXPORTS = ("moda_fwd", "moda_bwd", "moda_bwd_workspace_bytes", "moda_pack_depth",
+EXPORTS = ("moda_fwd", "moda_bwd", "moda_bwd_workspace_bytes", "moda_bwd_noalloc",
+           "moda_pack_depth",
            "moda_status_string", "moda_last_error", "moda_fwd_chunk_tokens", "moda_timing_arm",
            "moda_timing_count", "moda_timing_label")
 
@@ -60,6 +62,8 @@ def load(path: str = LIB_PATH):
         lib.moda_fwd.restype = I
         lib.moda_bwd.argtypes = [PP] + [P] * 14 + [ctypes.c_size_t, P]
         lib.moda_bwd.restype = I
+        lib.moda_bwd_noalloc.argtypes = [PP] + [P] * 14
+        lib.moda_bwd_noalloc.restype = I
         lib.moda_bwd_workspace_bytes.argtypes = [PP]
         lib.moda_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.moda_pack_depth.argtypes = [PP, P, P, P]
@@ -201,6 +205,24 @@ def moda_bwd(p: Problem, Q, K, V, Kd, Vd, O, lse, dO, dQ, dK, dV, dKd, dVd, work
                            _ptr(O), _ptr(lse), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV),
                            _ptr(dKd), _ptr(dVd), _ptr(workspace), int(workspace_bytes),
                            _stream(stream)))
+
+
+def moda_bwd_noalloc(p: Problem, Q, K, V, Kd, Vd, O, lse, dO, dQ, dK, dV, dKd, dVd,
+                     stream=None) -> None:
+    """moda_bwd with the library's static per-GPU scratch instead of a workspace (for
+    callers that cannot allocate); calls that overlap on one GPU race."""
+    dt = _TORCH_DTYPE.get(p.dtype)
+    if dt is not None:
+        q, kv, dep, rows = _shapes(p)
+        nodep = p.L == 0
+        _check_tensors([("Q", Q, q, dt), ("K", K, kv, dt), ("V", V, kv, dt),
+                        ("Kd", Kd, dep, dt, nodep), ("Vd", Vd, dep, dt, nodep),
+                        ("O", O, q, dt), ("lse", lse, rows, torch.float32), ("dO", dO, q, dt),
+                        ("dQ", dQ, q, dt), ("dK", dK, kv, dt), ("dV", dV, kv, dt),
+                        ("dKd", dKd, dep, dt, nodep), ("dVd", dVd, dep, dt, nodep)])
+    _check(load().moda_bwd_noalloc(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Kd),
+                                   _ptr(Vd), _ptr(O), _ptr(lse), _ptr(dO), _ptr(dQ), _ptr(dK),
+                                   _ptr(dV), _ptr(dKd), _ptr(dVd), _stream(stream)))
 
 
 def moda_pack_depth(p: Problem, layers, packed, stream=None) -> None:

@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "kernels.hpp"
 
@@ -141,6 +142,48 @@ size_t bwd_ws_bytes(const moda::Shape& s, int32_t dtype)
     return (n + 255) & ~size_t(255);
 }
 
+// ---- scratch of the no-allocation backward ----
+// One static device array per GPU (the code object's copy on that device), used by
+// moda_bwd_noalloc in place of the caller's workspace.  In host code the name
+// `scratch` is a host-side stand-in, not a device address; the address on each
+// device comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MODA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the current device, which `st` must belong to.
+moda_status_t device_scratch(hipStream_t st, void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MODA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (st) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(st, &sdev);
+        if (e != hipSuccess) return fail(MODA_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+        if (sdev != dev)
+            return fail(MODA_ERR_INVALID_ARGUMENT,
+                        "stream belongs to device %d, not to the current device %d", (int)sdev, dev);
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MODA_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* ptr = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = ptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess)
+        return fail(MODA_ERR_HIP, "hipGetSymbolAddress(scratch): %s",
+                    hipGetErrorString(g_scratch_err[dev]));
+    if (!g_scratch_ptr[dev]) return fail(MODA_ERR_HIP, "no device address for the scratch array");
+    *out = g_scratch_ptr[dev];
+    return MODA_OK;
+}
+
 constexpr int32_t kMaxTimedKernels = 4096;
 
 struct Timing {
@@ -151,6 +194,39 @@ struct Timing {
     int32_t nlabels = 0;
 };
 thread_local Timing g_timing;
+
+// Problem and pointer checks shared by the two backward entry points.
+moda_status_t check_bwd(const moda_problem_t* p, const void* Q, const void* K, const void* V,
+                        const void* Kd, const void* Vd, const void* O, const float* lse,
+                        const void* dO, void* dQ, void* dK, void* dV, void* dKd, void* dVd,
+                        moda::Shape* s)
+{
+    moda_status_t st = check_problem(p, true, s);
+    if (st != MODA_OK) return st;
+    const void* ptrs[] = {Q, K, V, O, lse, dO, dQ, dK, dV};
+    const char* names[] = {"Q", "K", "V", "O", "lse", "dO", "dQ", "dK", "dV"};
+    for (int i = 0; i < 9; ++i)
+        if ((st = check_ptr(ptrs[i], names[i])) != MODA_OK) return st;
+    if ((st = check_depth(p, Kd, "Kd", Vd, "Vd")) != MODA_OK) return st;
+    return check_depth(p, dKd, "dKd", dVd, "dVd");
+}
+
+moda_status_t launch_bwd(const moda_problem_t* p, const moda::Shape& s, const void* Q,
+                         const void* K, const void* V, const void* Kd, const void* Vd,
+                         const void* O, const float* lse, const void* dO, void* dQ, void* dK,
+                         void* dV, void* dKd, void* dVd, void* ws, hipStream_t hs)
+{
+    hipError_t e;
+    if (p->dtype == MODA_BF16)
+        e = moda::launch_bwd_bf16(s, Q, K, V, Kd, Vd, O, lse, dO, dQ, dK, dV, dKd, dVd,
+                                  (float*)ws, hs);
+    else
+        e = moda::launch_bwd_f32(s, (const float*)Q, (const float*)K, (const float*)V,
+                                 (const float*)Kd, (const float*)Vd, (const float*)O, lse,
+                                 (const float*)dO, (float*)dQ, (float*)dK, (float*)dV,
+                                 (float*)dKd, (float*)dVd, (float*)ws, hs);
+    return hip_status(e, "moda_bwd launch");
+}
 
 }  // namespace
 
@@ -252,14 +328,8 @@ moda_status_t moda_bwd(const moda_problem_t* p, const void* Q, const void* K, co
                        void* workspace, size_t workspace_bytes, void* stream)
 {
     moda::Shape s;
-    moda_status_t st = check_problem(p, true, &s);
+    moda_status_t st = check_bwd(p, Q, K, V, Kd, Vd, O, lse, dO, dQ, dK, dV, dKd, dVd, &s);
     if (st != MODA_OK) return st;
-    const void* ptrs[] = {Q, K, V, O, lse, dO, dQ, dK, dV};
-    const char* names[] = {"Q", "K", "V", "O", "lse", "dO", "dQ", "dK", "dV"};
-    for (int i = 0; i < 9; ++i)
-        if ((st = check_ptr(ptrs[i], names[i])) != MODA_OK) return st;
-    if ((st = check_depth(p, Kd, "Kd", Vd, "Vd")) != MODA_OK) return st;
-    if ((st = check_depth(p, dKd, "dKd", dVd, "dVd")) != MODA_OK) return st;
     if (!workspace) return fail(MODA_ERR_INVALID_ARGUMENT, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace) & 255u)
         return fail(MODA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
@@ -267,17 +337,29 @@ moda_status_t moda_bwd(const moda_problem_t* p, const void* Q, const void* K, co
     if (workspace_bytes < need)
         return fail(MODA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu required",
                     workspace_bytes, need);
+    return launch_bwd(p, s, Q, K, V, Kd, Vd, O, lse, dO, dQ, dK, dV, dKd, dVd, workspace,
+                      reinterpret_cast<hipStream_t>(stream));
+}
+
+moda_status_t moda_bwd_noalloc(const moda_problem_t* p, const void* Q, const void* K,
+                               const void* V, const void* Kd, const void* Vd, const void* O,
+                               const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                               void* dKd, void* dVd, void* stream)
+{
+    moda::Shape s;
+    moda_status_t st = check_bwd(p, Q, K, V, Kd, Vd, O, lse, dO, dQ, dK, dV, dKd, dVd, &s);
+    if (st != MODA_OK) return st;
+    const size_t need = bwd_ws_bytes(s, p->dtype);
+    if (need > MODA_NOALLOC_SCRATCH_BYTES)
+        return fail(MODA_ERR_UNSUPPORTED,
+                    "problem needs %zu bytes of scratch; moda_bwd_noalloc has %zu (use moda_bwd)",
+                    need, (size_t)MODA_NOALLOC_SCRATCH_BYTES);
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e;
-    if (p->dtype == MODA_BF16)
-        e = moda::launch_bwd_bf16(s, Q, K, V, Kd, Vd, O, lse, dO, dQ, dK, dV, dKd, dVd,
-                                  (float*)workspace, hs);
-    else
-        e = moda::launch_bwd_f32(s, (const float*)Q, (const float*)K, (const float*)V,
-                                 (const float*)Kd, (const float*)Vd, (const float*)O, lse,
-                                 (const float*)dO, (float*)dQ, (float*)dK, (float*)dV,
-                                 (float*)dKd, (float*)dVd, (float*)workspace, hs);
-    return hip_status(e, "moda_bwd launch");
+    void* ws = nullptr;
+    if ((st = device_scratch(hs, &ws)) != MODA_OK) return st;
+    // The kernels write every scratch value they read (per-row lse and D first, then
+    // the depth part of dQ), so nothing needs clearing between calls.
+    return launch_bwd(p, s, Q, K, V, Kd, Vd, O, lse, dO, dQ, dK, dV, dKd, dVd, ws, hs);
 }
 
 moda_status_t moda_pack_depth(const moda_problem_t* p, const void* layers, void* packed,
