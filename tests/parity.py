@@ -73,14 +73,14 @@ def to64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_fwd(x, w, chunk=0):
+def run_fwd(x, w, chunk=0, causal=True, window=0):
     return binding.fwd(x["Q"], x["K"], x["V"], x.get("Kd"), x.get("Vd"), w.L, w.scale,
-                       chunk=chunk)
+                       chunk=chunk, causal=causal, window=window)
 
 
-def run_bwd(x, w, O, lse, chunk=0):
+def run_bwd(x, w, O, lse, chunk=0, causal=True, window=0):
     return binding.bwd(x["Q"], x["K"], x["V"], x.get("Kd"), x.get("Vd"), O, lse, x["dO"], w.L,
-                       w.scale, chunk=chunk)
+                       w.scale, chunk=chunk, causal=causal, window=window)
 
 
 def oracle_inputs(x):

@@ -24,33 +24,35 @@ DEV = "cuda:0"
 W = inputs.WORKLOADS
 
 
-def abs_terms(w, x):
+def abs_terms(w, x, causal=True, window=0):
     """Absolute-term sums of every output (oracle.brute), for the edge-shape bound."""
     f = {k: (to64(v) if v is not None else None) for k, v in x.items()}
     return brute.abs_terms(f["Q"], f["K"], f["V"], f.get("Kd"), f.get("Vd"), f.get("dO"), w.L,
-                           w.scale)
+                           w.scale, causal, window)
 
 
-def fwd_full_check(w, x, chunk=0, label="", edge=False):
-    O, lse = run_fwd(x, w, chunk)
+def fwd_full_check(w, x, chunk=0, label="", edge=False, causal=True, window=0):
+    O, lse = run_fwd(x, w, chunk, causal, window)
     torch.cuda.synchronize()
     h = oracle_inputs(x)
-    Or, lr = oracle.fwd(h["Q"], h["K"], h["V"], h.get("Kd"), h.get("Vd"), w.L, w.scale)
-    A = abs_terms(w, x) if edge else {}
+    Or, lr = oracle.fwd(h["Q"], h["K"], h["V"], h.get("Kd"), h.get("Vd"), w.L, w.scale,
+                        causal, window)
+    A = abs_terms(w, x, causal, window) if edge else {}
     check(f"{w.name}{label} O", to64(O), Or, w.dtype, edge=edge, terms=A.get("O"))
     check(f"{w.name}{label} lse", to64(lse), lr, w.dtype, edge=edge, fp32_output=True)
     return O, lse
 
 
-def bwd_full_check(w, x, O, lse, chunk=0, label="", edge=False):
-    dQ, dK, dV, dKd, dVd = run_bwd(x, w, O, lse, chunk)
+def bwd_full_check(w, x, O, lse, chunk=0, label="", edge=False, causal=True, window=0):
+    dQ, dK, dV, dKd, dVd = run_bwd(x, w, O, lse, chunk, causal, window)
     torch.cuda.synchronize()
     h = oracle_inputs(x)
-    g = oracle.bwd(h["Q"], h["K"], h["V"], h.get("Kd"), h.get("Vd"), h["dO"], w.L, w.scale)
+    g = oracle.bwd(h["Q"], h["K"], h["V"], h.get("Kd"), h.get("Vd"), h["dO"], w.L, w.scale,
+                   causal, window)
     got = {"dQ": dQ, "dK": dK, "dV": dV}
     if w.L > 0:
         got.update(dKd=dKd, dVd=dVd)
-    A = abs_terms(w, x) if edge else {}
+    A = abs_terms(w, x, causal, window) if edge else {}
     for k, v in got.items():
         check(f"{w.name}{label} {k}", to64(v), g[k], w.dtype, edge=edge, terms=A.get(k))
 
@@ -399,6 +401,84 @@ def test_outputs_stay_inside_their_buffers():
     torch.cuda.synchronize()
     for buf in [ob, lb] + [g[0] for g in grads]:
         assert torch.all(buf[:pad] == guard) and torch.all(buf[-pad:] == guard)
+
+
+# ---------------- variants: non-causal, sliding-window depth ----------------
+
+VARIANT_SHAPES = [
+    # B, Hq, Hk, T, d, L
+    (1, 4, 2, 77, 128, 5),      # ragged T
+    (2, 8, 8, 130, 64, 3),      # G = 1
+    (1, 32, 1, 50, 128, 2),     # G = 32
+    (1, 16, 2, 333, 128, 7),    # G = 8, ragged
+    (1, 2, 1, 33, 64, 40),      # a token's depth rows span two 32-row blocks
+]
+VARIANTS = [(False, 0), (True, 1), (True, -1), (False, 2)]   # (causal, window); -1: L - 1
+
+
+@pytest.mark.parametrize("shape", VARIANT_SHAPES, ids=lambda s: "B{}Hq{}Hk{}T{}d{}L{}".format(*s))
+@pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: f"causal{int(v[0])}-W{v[1]}")
+@pytest.mark.parametrize("chunk", [0, 16])
+def test_variant_shapes_forward_backward(shape, variant, chunk):
+    """Non-causal MoDA (every sequence key visible; the depth matching mask kept) and the
+    sliding-window depth slots (the last W of L), forward and all five gradients against
+    the oracle in full."""
+    B, Hq, Hk, T, d, L = shape
+    causal, W = variant
+    W = L - 1 if W < 0 else min(W, L)
+    w = inputs.Workload("variant", B, Hq, Hk, T, d, L, chunk=chunk, dtype="bf16")
+    x = inputs.make(w, seed=sum(shape) + 3 * W + int(causal), device=DEV,
+                    names=("Q", "K", "V", "Kd", "Vd", "dO"))
+    tag = f" {shape} causal={causal} W={W} c{chunk}"
+    O, lse = fwd_full_check(w, x, chunk, label=tag, edge=True, causal=causal, window=W)
+    bwd_full_check(w, x, O, lse, chunk, label=tag, edge=True, causal=causal, window=W)
+
+
+@pytest.mark.parametrize("variant", [(False, 0), (True, 2), (False, 1)])
+def test_fp32_variants(variant):
+    causal, W = variant
+    w = inputs.Workload("variant_f32", 1, 4, 2, 37, 64, 3, chunk=0, dtype="f32")
+    x = inputs.make(w, seed=50 + W, device=DEV, names=("Q", "K", "V", "Kd", "Vd", "dO"))
+    O, lse = fwd_full_check(w, x, causal=causal, window=W, label=f" causal={causal} W={W}")
+    bwd_full_check(w, x, O, lse, causal=causal, window=W, label=f" causal={causal} W={W}")
+
+
+def test_noncausal_small_model_forward_full_and_two_kv_groups_backward():
+    """The small-model workload (T = 2048, G = 2, d = 64, L = 16) without the sequence
+    causal mask, at the plain bound: the whole forward, and all five gradients of two KV
+    groups."""
+    w = W["small_model"].with_(bwd=True)
+    x = inputs.make(w, seed=13, device=DEV, names=("Q", "K", "V", "Kd", "Vd", "dO"))
+    O, lse = fwd_full_check(w, x, label=" non-causal", causal=False)
+    dQ, dK, dV, dKd, dVd = run_bwd(x, w, O, lse, causal=False)
+    torch.cuda.synchronize()
+    h = oracle_inputs(x)
+    G = w.G
+    for b, kv in ((0, 0), (1, 7)):
+        g = oracle.bwd_group(h["Q"], h["K"], h["V"], h["Kd"], h["Vd"], h["dO"], w.L, w.scale,
+                             b, kv, causal=False)
+        hs = slice(kv * G, (kv + 1) * G)
+        tag = f"{w.name} non-causal (b={b}, kv={kv})"
+        for name, got in (("dQ", dQ[b, hs]), ("dK", dK[b, kv]), ("dV", dV[b, kv]),
+                          ("dKd", dKd[b, kv]), ("dVd", dVd[b, kv])):
+            check(f"{tag} {name}", to64(got), g[name], w.dtype)
+
+
+def test_window_layer_1p5b_forward_one_kv_group():
+    """The 1.5B-like layer (T = 8192, G = 4, d = 128, L = 32) seeing only the last 8 depth
+    slots: one full KV group of the forward at the plain bound."""
+    w = W["layer_1p5b_8k"]
+    x = inputs.make(w, seed=14, device=DEV)
+    O, lse = run_fwd(x, w, window=8)
+    torch.cuda.synchronize()
+    h = oracle_inputs(x)
+    kv = 1
+    rows = rows_array(1, w.Hq, range(w.T), heads=range(kv * w.G, (kv + 1) * w.G))
+    Or, lr = oracle.fwd_rows(h["Q"], h["K"], h["V"], h["Kd"], h["Vd"], w.L, w.scale, rows,
+                             window=8)
+    check(f"{w.name} W=8 O (kv group {kv})", gather_rows(O, rows), Or, w.dtype)
+    check(f"{w.name} W=8 lse (kv group {kv})", gather_rows(lse, rows)[:, None], lr[:, None],
+          w.dtype, fp32_output=True)
 
 
 # ---------------- depth packer ----------------

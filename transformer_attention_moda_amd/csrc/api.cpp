@@ -89,12 +89,12 @@ moda_status_t check_problem(const moda_problem_t* p, bool need_head_dim, moda::S
         return fail(MODA_ERR_UNSUPPORTED,
                     "(G-1)*T = %lld rows of d = %lld exceed the 2 GiB reach of the staging offsets",
                     (long long)((G - 1) * p->T), (long long)p->d);
-    if (p->flags != 0 || (p->window != 0 && p->window != p->L))
-        return fail(MODA_ERR_UNSUPPORTED, "non-causal or windowed depth not built yet");
     if (s) {
         s->B = p->B; s->Hq = p->Hq; s->Hk = p->Hk; s->T = p->T; s->d = p->d; s->L = p->L;
         s->scale = p->scale;
         s->G = (int)G;
+        s->noncausal = (p->flags & MODA_NONCAUSAL) != 0;
+        s->W = p->window > 0 ? p->window : (int)p->L;
     }
     return MODA_OK;
 }

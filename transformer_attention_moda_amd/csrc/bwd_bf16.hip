@@ -22,6 +22,12 @@
 //              operands and walks the query rows that see them:
 //              S = Q K^T, dP = dO V^T (lane = key), dV^T += dO^T P and
 //              dK^T += Q^T dS with dO and Q read transposed from LDS.
+//
+// Variants.  Non-causal (runtime flag): every key is visible to every query, so
+// bwd_dq walks all key tiles and bwd_dkdv all query rows, masking only ragged
+// ends.  A depth window (the last W of L slots): bwd_depth gives the hidden
+// slots weight 0, so their dKd, dVd rows are written as exact zeros and they add
+// nothing to dQ.
 #include <type_traits>
 
 #include "common.hpp"
@@ -48,6 +54,8 @@ struct BwdArgs {
     float* Dv;     // <dO, O>,        [B*Hq*T]
     float* dqd;    // depth part of dQ / scale, fp32 [B*Hq*T][d] (L > 0)
     int Hq, Hk, T, L, G, lgG;
+    int W;         // visible depth slots per token (the last W of L)
+    int noncausal; // every sequence key visible
     int nblocks;   // work blocks per (b, kv) of the launched kernel
     float c;       // scale * log2(e)
     float scale;
@@ -110,13 +118,15 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
     const int b = unit / a.Hk, kv = unit % a.Hk;
     const int64_t TG = (int64_t)T * G;
     const int64_t r0 = (int64_t)chunk * BM;
-    const int t_hi_wg = (int)min((r0 + BM - 1) / G, (int64_t)T - 1);
+    const bool nc = a.noncausal != 0;
+    const int t_hi_wg = nc ? T - 1 : (int)min((r0 + BM - 1) / G, (int64_t)T - 1);
     const int64_t fw = r0 + 32 * w, fcol = fw + col;
     const bool valid = fcol < TG;
     const int tcol = (int)min(fcol / G, (int64_t)T - 1);
     const int hq = kv * G + (int)(fcol % G);
-    const int tw_lo = (int)min(fw / G, (int64_t)T - 1);
-    const int tw_hi = (int)min((fw + 31) / G, (int64_t)T - 1);
+    // Keys up to vis_lo are visible to every lane of the wave, keys up to vis_hi to some.
+    const int vis_lo = nc ? T - 1 : (int)min(fw / G, (int64_t)T - 1);
+    const int vis_hi = nc ? T - 1 : (int)min((fw + 31) / G, (int64_t)T - 1);
 
     const int64_t kvbase = ((int64_t)b * a.Hk + kv) * T;
     const uint16_t* Kb = a.K + kvbase * D;
@@ -150,7 +160,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
         sofs[i2] = r * D + ((lane % TL::CPR) ^ TL::swz(r)) * 8;
     }
     const int ntiles = t_hi_wg / BN + 1;
-    const int t_lo_wg = (int)min(r0 / G, (int64_t)T - 1);
+    const int t_lo_wg = nc ? T - 1 : (int)min(r0 / G, (int64_t)T - 1);
     const int n_full = (t_lo_wg + 1) / BN;     // tiles no wave of this workgroup needs to mask
     auto stage = [&](int tile, uint16_t* ks) {
         uint16_t* const vs = ks + ELEMS;
@@ -177,7 +187,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
         const uint16_t* vs = ks + ELEMS;
         if (it + 1 < ntiles) stage(it + 1, BUF ? lb0 : lb1);
         const int k0 = it * BN;
-        if (!MASKED || k0 <= tw_hi) {
+        if (!MASKED || k0 <= vis_hi) {
             f32x16 sv[2], dp[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -197,7 +207,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
                 SCHED_GROUP(kSchedDsRead, 1);
             }
             SCHED_GROUP(kSchedMfma, 4);
-            const bool need_mask = MASKED && k0 + BN - 1 > tw_lo;
+            const bool need_mask = MASKED && k0 + BN - 1 > vis_lo;
+            const int lim = nc ? T - 1 : tcol;   // last key this lane sees
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -205,7 +216,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
                     float pr = fast_exp2(fmaf(sv[kb][j], c, -lse2));
                     if (MASKED) {
                         const int key = k0 + kb * 32 + (j >> 2) * 8 + hf * 4 + (j & 3);
-                        if (need_mask && key > tcol) pr = 0.f;
+                        if (need_mask && key > lim) pr = 0.f;
                     }
                     sv[kb][j] = pr * (dp[kb][j] - Dr);
                 }
@@ -308,9 +319,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
     lo.init(lane);
 
     const int64_t TG = (int64_t)T * G;
-    const int64_t f_start = (int64_t)k0 * G;   // first folded row that sees a key of this block
+    const bool nc = a.noncausal != 0;
+    // First folded row that sees a key of this block, and the leading tiles that hold rows
+    // not seeing some key of it (causal only: non-causal rows see every key).
+    const int64_t f_start = nc ? 0 : (int64_t)k0 * G;
     const int ntiles = (int)((TG - f_start + BQ - 1) / BQ);
-    const int n_mask = min(ntiles, ((BK - 1) * G + BQ - 1) / BQ);   // tiles reaching below key k0+BK-1
+    const int n_mask = nc ? 0 : min(ntiles, ((BK - 1) * G + BQ - 1) / BQ);
     const int64_t qhead0 = (int64_t)b * a.Hq + (int64_t)kv * G;
 
     // Folded row f0 + r (f0 a multiple of BQ, G | BQ) is query head qhead0 + r%G at token
@@ -573,9 +587,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_depth_kernel(BwdArgs a)
             vb[buf][si] = __builtin_bit_cast(bf16x8, ld16(vrow + 16 * si));
         }
     };
+    const int hidden = L - a.W;   // slots 0 .. hidden-1 of each token are outside the window
     auto block = [&](int64_t rb, const bf16x8 (&kr)[D / 16], const bf16x8 (&vr)[D / 16]) {
         const int64_t r = rb + col;                          // this lane's depth row
         const int rtok = (int)(min(r, TL_rows - 1) / L);
+        const bool shown = (int)(r - (int64_t)rtok * L) >= hidden;
         f32x16 s, dp;
 #pragma unroll
         for (int j = 0; j < 16; ++j) s[j] = dp[j] = 0.f;
@@ -595,7 +611,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_depth_kernel(BwdArgs a)
                 const int j = 4 * jj + e;
                 const int tq = (int)((fw + jj * 8 + 4 * hf + e) >> lgG);
                 float p = fast_exp2(fmaf(s[j], c, -lv[e]));
-                if (tq != rtok || r >= dhi) p = 0.f;
+                if (tq != rtok || r >= dhi || !shown) p = 0.f;
                 s[j] = p;
                 dp[j] = p * (dp[j] - dvv[e]);
             }
@@ -728,6 +744,8 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* Q, const void* K, const v
     a.T = (int)s.T;
     a.L = (int)s.L;
     a.G = s.G;
+    a.W = s.W;
+    a.noncausal = s.noncausal ? 1 : 0;
     a.lgG = 0;
     while ((1 << a.lgG) < s.G) ++a.lgG;
     a.c = s.scale * kLog2e;

@@ -26,6 +26,13 @@
 //
 // Epilogue: O = o / sum in bf16 (round to nearest even) and
 // lse = scale*m + ln(sum) in fp32.
+//
+// Variants.  Non-causal (a runtime flag): every key 0..T-1 is visible, so every
+// tile but a ragged last one skips the mask.  A depth window of the last W of L
+// slots (a template instance of its own, so the full-depth kernel is unchanged):
+// the depth phase gathers only the visible rows, W per token, into its 32-row
+// blocks ("virtual rows" v -> token tw_lo + v / W, slot L - W + v % W), so it
+// reads W/L of the depth bytes.
 #include <type_traits>
 
 #include "common.hpp"
@@ -43,6 +50,8 @@ struct FwdArgs {
     uint16_t* O;
     float* lse;
     int Hq, Hk, T, L, G;
+    int W;         // visible depth slots per token (the last W of L)
+    int noncausal; // every sequence key visible
     int nchunks;   // query chunks per (b, kv)
     float c;       // scale * log2(e)
     float scale;
@@ -108,7 +117,7 @@ __device__ __forceinline__ float row_sum_bf16(const bf16x8& p, float acc)
 
 // Eight waves per CU either way: one 8-wave workgroup (256 rows) or two 4-wave
 // workgroups (128 rows), two waves per SIMD and at most 256 registers per wave.
-template <int D, int NW>
+template <int D, int NW, bool WIN>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
 {
     using TL = LdsTile<D>;
@@ -131,7 +140,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
     const int b = unit / a.Hk, kv = unit % a.Hk;
     const int64_t TG = (int64_t)T * G;
     const int64_t r0 = (int64_t)chunk * BM;
-    const int t_hi_wg = (int)min((r0 + BM - 1) / G, (int64_t)T - 1);
+    const bool nc = a.noncausal != 0;
+    // Last key any query of the workgroup sees.
+    const int t_hi_wg = nc ? T - 1 : (int)min((r0 + BM - 1) / G, (int64_t)T - 1);
 
     const int64_t fw = r0 + 32 * w;              // first folded row of this wave
     const int64_t fcol = fw + col;               // this lane's column
@@ -140,6 +151,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
     const int hq = kv * G + (int)(fcol % G);
     const int tw_lo = (int)min(fw / G, (int64_t)T - 1);
     const int tw_hi = (int)min((fw + 31) / G, (int64_t)T - 1);
+    // Keys up to vis_lo are visible to every lane of the wave, keys up to vis_hi to some.
+    const int vis_lo = nc ? T - 1 : tw_lo;
+    const int vis_hi = nc ? T - 1 : tw_hi;
 
     const int64_t kvbase = ((int64_t)b * a.Hk + kv) * T;
     const uint16_t* Kb = a.K + kvbase * D;
@@ -167,29 +181,51 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
     float m = -1e30f, l = 0.f;
 
     // ---- depth rows of this wave's tokens ----
-    // Rows [tw_lo*L, (tw_hi+1)*L) of the token-major depth KV, in blocks of 32.  A
-    // block's K rows are MFMA A operands loaded straight into registers, its V rows go
-    // to the wave's LDS slice (direct loads) for the transposed read.  Prefetch: the
-    // next block's K loads are issued as soon as the current scores have consumed the
-    // registers, its V loads as soon as the current PV has read the slice.  Mask: row r
-    // is visible to token t iff t*L <= r < t*L + L.
+    // The visible depth rows of tokens tw_lo..tw_hi, in blocks of 32: all of
+    // [tw_lo*L, (tw_hi+1)*L) without a window; with one, W rows per token gathered as
+    // virtual rows v (token tw_lo + v / W, slot L - W + v % W).  A block's K rows are
+    // MFMA A operands loaded straight into registers, its V rows go to the wave's LDS
+    // slice (direct loads) for the transposed read.  Prefetch: the next block's K loads
+    // are issued as soon as the current scores have consumed the registers, its V loads
+    // as soon as the current PV has read the slice.  Mask: virtual row v is visible to
+    // token t iff (t - tw_lo)*W <= v < (t - tw_lo)*W + W.
     auto depth_phase = [&]() {
         const int64_t TL_rows = (int64_t)T * L;
         const uint16_t* Kdb = a.Kd + kvbase * (int64_t)L * D;
         const uint16_t* Vdb = a.Vd + kvbase * (int64_t)L * D;
-        const int64_t dlo = (int64_t)tw_lo * L, dhi = (int64_t)(tw_hi + 1) * L;
-        const int nblk = (int)((dhi - dlo + 31) / 32);
+        const int Wn = WIN ? a.W : L;
+        const int64_t dlo = (int64_t)tw_lo * L;
+        const int64_t nv = (int64_t)(tw_hi - tw_lo + 1) * Wn;   // virtual rows of the wave
+        const int nblk = (int)((nv + 31) / 32);
+        // Depth row of virtual row v (v < nv).
+        auto phys = [&](int64_t v) -> int64_t {
+            if constexpr (!WIN) {
+                return dlo + v;
+            } else {
+                const uint32_t vv = (uint32_t)v, tok = vv / (uint32_t)Wn;
+                return (int64_t)(tw_lo + (int)tok) * L + (L - Wn) + (int)(vv - tok * (uint32_t)Wn);
+            }
+        };
         uint16_t* const arr = (w >> 1) == 0 ? lk0 : (w >> 1) == 1 ? lv0 : (w >> 1) == 2 ? lk1 : lv1;
         uint16_t* const slot = arr + (w & 1) * 32 * D;
         constexpr int NK = D / 16;                     // K loads per block (vector-memory instructions)
         bf16x8 kr[D / 16];
-        auto issue_v = [&](int i) {   // rows past the end repeat the last row (weight 0)
-            const int64_t rb = dlo + 32 * (int64_t)i;
-            stage_rows<D>(slot, 32, Vdb + rb * D, [&](int r) { return (int)(min(rb + r, TL_rows - 1) - rb) * D; },
-                          lane, 0, 1);
+        auto issue_v = [&](int i) {   // rows past the wave's last visible row repeat a row (weight 0)
+            const int64_t vb = 32 * (int64_t)i;
+            if constexpr (!WIN) {
+                const int64_t rb = dlo + vb;
+                stage_rows<D>(slot, 32, Vdb + rb * D,
+                              [&](int r) { return (int)(min(rb + r, TL_rows - 1) - rb) * D; }, lane, 0, 1);
+            } else {
+                const int64_t rb = phys(vb);
+                stage_rows<D>(slot, 32, Vdb + rb * D,
+                              [&](int r) { return (int)(phys(min(vb + r, nv - 1)) - rb) * D; }, lane, 0, 1);
+            }
         };
         auto issue_k = [&](int i) {
-            const uint16_t* krow = Kdb + min(dlo + 32 * (int64_t)i + col, TL_rows - 1) * D + 8 * hf;
+            const int64_t v = 32 * (int64_t)i + col;
+            const int64_t r = WIN ? phys(min(v, nv - 1)) : min(dlo + v, TL_rows - 1);
+            const uint16_t* krow = Kdb + r * D + 8 * hf;
 #pragma unroll
             for (int si = 0; si < D / 16; ++si) kr[si] = __builtin_bit_cast(bf16x8, ld16(krow + 16 * si));
         };
@@ -205,11 +241,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
 #pragma unroll
             for (int si = 0; si < D / 16; ++si) s[0] = mfma32(kr[si], qreg[si], s[0]);
             if (more) issue_k(i + 1);
-            const int64_t lo = (int64_t)tcol * L - dlo - 32 * (int64_t)i - 4 * hf;   // first visible row
+            // first visible virtual row of this lane's token, relative to the lane's rows
+            const int64_t lo = (int64_t)(tcol - tw_lo) * Wn - 32 * (int64_t)i - 4 * hf;
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int rj = (j >> 2) * 8 + (j & 3);
-                if (rj < lo || rj >= lo + L) s[0][j] = -INFINITY;
+                if (rj < lo || rj >= lo + Wn) s[0][j] = -INFINITY;
             }
             softmax_update<D, 1>(s, m, l, o, a.c);
             if (more) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NK) : "memory");   // V of block i landed
@@ -246,7 +283,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
         sofs[i] = r * D + ((lane % TL::CPR) ^ TL::swz(r)) * 8;
     }
     const int ntiles = t_hi_wg / BN + 1;
-    const int t_lo_wg = (int)min(r0 / G, (int64_t)T - 1);
+    // Last key every query of the workgroup sees: tiles wholly at or below it need no mask.
+    const int t_lo_wg = nc ? T - 1 : (int)min(r0 / G, (int64_t)T - 1);
     const int n_full = (t_lo_wg + 1) / BN;     // tiles no wave of this workgroup needs to mask
 
     auto stage = [&](int tile, uint16_t* ks, uint16_t* vs) {
@@ -279,7 +317,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
             else stage(it + 1, lk1, lv1);
         }
         const int k0 = it * BN;
-        if (!MASKED || k0 <= tw_hi) {
+        if (!MASKED || k0 <= vis_hi) {
             f32x16 s[2];
 #pragma unroll
             for (int j = 0; j < 16; ++j) s[0][j] = s[1][j] = 0.f;
@@ -298,13 +336,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
                 SCHED_GROUP(kSchedDsRead, 1);
             }
             SCHED_GROUP(kSchedMfma, 4);
-            if (MASKED && k0 + BN - 1 > tw_lo) {
+            if (MASKED && k0 + BN - 1 > vis_lo) {
+                const int lim = nc ? T - 1 : tcol;   // last key this lane sees
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
                         const int key = k0 + kb * 32 + (j >> 2) * 8 + hf * 4 + (j & 3);
-                        if (key > tcol) s[kb][j] = -INFINITY;
+                        if (key > lim) s[kb][j] = -INFINITY;
                     }
             }
             softmax_update<D, 2, false>(s, m, l, o, a.c);
@@ -380,7 +419,12 @@ hipError_t launch(const Shape& s, const FwdArgs& a, int nunits, hipStream_t st)
 {
     const int64_t grid = (int64_t)nunits * a.nchunks;
     timing_begin("fwd", st);
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, st, a);
+    if (a.L > 0 && a.W < a.L)
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, true>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                           st, a);
+    else
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, false>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                           st, a);
     timing_end(st);
     return hipGetLastError();
 }
@@ -404,6 +448,8 @@ hipError_t launch_fwd_bf16(const Shape& s, const void* Q, const void* K, const v
     a.T = (int)s.T;
     a.L = (int)s.L;
     a.G = s.G;
+    a.W = s.W;
+    a.noncausal = s.noncausal ? 1 : 0;
     a.scale = s.scale;
     a.c = s.scale * kLog2e;
     const int64_t TG = s.T * s.G;

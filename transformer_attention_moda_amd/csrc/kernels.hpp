@@ -15,6 +15,8 @@ struct Shape {
     int64_t B, Hq, Hk, T, d, L;
     float scale;
     int G;
+    bool noncausal;  // every sequence key visible to every query
+    int W;           // visible depth slots per token: the last W of L (W == L: all)
 };
 
 // Forward, bfloat16 storage, MFMA.  rows_per_wg is 128 or 256 folded query rows.

@@ -6,7 +6,9 @@
 // kernels carry no tiling: they are the straightforward GPU form of the
 // operator ("Mixture-of-Depths Attention", arXiv 2603.15619, paper summary,
 // section 3.4, MoDA equation with the sequence causal and depth matching
-// masks) and of its derivative, used where fp32 storage is requested.
+// masks) and of its derivative, used where fp32 storage is requested.  The
+// variants: non-causal (every key visible) and a depth window (the last W of a
+// token's L slots visible; the hidden slots get zero gradient).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -41,6 +43,8 @@ struct RowArgs {
     void* dVd;
     float* Dws;
     int B, Hq, Hk, T, L, G;
+    int W;          // visible depth slots per token (the last W of L)
+    int noncausal;  // every sequence key visible
     float scale;
 };
 
@@ -80,10 +84,11 @@ __global__ __launch_bounds__(WPB * 64) void fwd_rows(RowArgs a)
         for (int i = 0; i < PE; ++i) o[i] = o[i] * alpha + p * ldf(v, lane + 64 * i);
         m = m_new;
     };
-    for (int j = 0; j <= t; ++j) visit(K + (int64_t)j * D, V + (int64_t)j * D);
+    const int last = a.noncausal ? a.T - 1 : t;
+    for (int j = 0; j <= last; ++j) visit(K + (int64_t)j * D, V + (int64_t)j * D);
     if (a.L > 0) {
         const int64_t base = (((int64_t)b * a.Hk + kv) * a.T + t) * a.L * D;
-        for (int j = 0; j < a.L; ++j)
+        for (int j = a.L - a.W; j < a.L; ++j)
             visit((const E*)a.Kd + base + (int64_t)j * D, (const E*)a.Vd + base + (int64_t)j * D);
     }
 #pragma unroll
@@ -144,8 +149,9 @@ __global__ __launch_bounds__(WPB * 64) void bwd_token(RowArgs a)
 #pragma unroll
             for (int i = 0; i < PE; ++i) dq[i] += a.scale * ds * ldf(k, lane + 64 * i);
         };
-        for (int j = 0; j <= t; ++j) visit(K + (int64_t)j * D, V + (int64_t)j * D);
-        for (int j = 0; j < a.L; ++j)
+        const int last = a.noncausal ? a.T - 1 : t;
+        for (int j = 0; j <= last; ++j) visit(K + (int64_t)j * D, V + (int64_t)j * D);
+        for (int j = a.L - a.W; j < a.L; ++j)
             visit((const E*)a.Kd + dbase + (int64_t)j * D, (const E*)a.Vd + dbase + (int64_t)j * D);
 #pragma unroll
         for (int i = 0; i < PE; ++i) stf((E*)a.dQ, row * D + lane + 64 * i, dq[i]);
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(WPB * 64) void bwd_token(RowArgs a)
         float dk[PE], dv[PE];
 #pragma unroll
         for (int i = 0; i < PE; ++i) dk[i] = dv[i] = 0.f;
-        for (int g = 0; g < a.G; ++g) {
+        for (int g = 0; g < a.G && j >= a.L - a.W; ++g) {   // hidden slots: zero gradient
             const int64_t row = ((int64_t)b * a.Hq + kv * a.G + g) * a.T + t;
             float s = 0.f, dp = 0.f, q[PE], dob[PE];
 #pragma unroll
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(WPB * 64) void bwd_key(RowArgs a)
     }
     for (int g = 0; g < a.G; ++g) {
         const int64_t rb = ((int64_t)b * a.Hq + kv * a.G + g) * a.T;
-        for (int t = j; t < a.T; ++t) {
+        for (int t = a.noncausal ? 0 : j; t < a.T; ++t) {
             const int64_t row = rb + t;
             float s = 0.f, dp = 0.f, q[PE], dob[PE];
 #pragma unroll
@@ -271,6 +277,8 @@ RowArgs make_args(const Shape& s)
     a.T = (int)s.T;
     a.L = (int)s.L;
     a.G = s.G;
+    a.W = s.W;
+    a.noncausal = s.noncausal ? 1 : 0;
     a.scale = s.scale;
     return a;
 }
