@@ -153,6 +153,42 @@ moda_status_t moda_bwd_noalloc(const moda_problem_t* p, const void* Q, const voi
                                void* dKd, void* dVd, void* stream);
 
 /*
+ * Decoding step: one new query token per (batch, query head) at cache position
+ * pos, against a cache of T tokens.  q [B, Hq, d]; K, V [B, Hk, T, d] hold the
+ * sequence keys, those at positions 0..pos visible (every one of the T with
+ * MODA_NONCAUSAL); Kd, Vd [B, Hk, T*L, d] hold the depth rows, of which the
+ * query sees its own, rows pos*L + L-W .. pos*L + L-1 (W = window, or L).
+ * Writes O [B, Hq, d] and lse [B, Hq]: exactly the forward's row at token pos
+ * for the sequence that ends there (the decoding step of the paper summary's
+ * "Complexity Analysis": per layer O(T d) for the sequence keys and O(L d) for
+ * the depth keys).  MODA_BF16 only.  The keys are split over many workgroups
+ * whose partial softmax states are merged through `workspace`: caller-owned
+ * device memory of at least moda_decode_workspace_bytes(p) bytes, 256-byte
+ * aligned (enough for any pos), not shared by concurrent calls.  Errors as for
+ * moda_fwd, plus MODA_ERR_INVALID_ARGUMENT for pos outside 0..T-1 or a NULL,
+ * misaligned or short workspace, and MODA_ERR_UNSUPPORTED for MODA_F32.
+ */
+size_t moda_decode_workspace_bytes(const moda_problem_t* p);
+
+moda_status_t moda_decode(const moda_problem_t* p, int64_t pos, const void* q, const void* K,
+                          const void* V, const void* Kd, const void* Vd, void* O, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Append-mode depth cache (the DepthKVCache of the PyPI page's architecture
+ * list, "contiguous depth KV storage across layers"): writes one layer's entries
+ * for tokens t0 .. t0+n-1, layer [B, Hk, n, d], into slot `slot` of the packed
+ * token-major cache packed [B, Hk, T*L, d]: row (t0+i)*L + slot of each (b, kv)
+ * block becomes layer[b, kv, i]; no other row is touched.  Appending layer l
+ * into slot l for l = 0..L-1 over all tokens builds what moda_pack_depth builds
+ * from the stacked layers.  A bitwise copy in p->dtype.  Requires L >= 1,
+ * 0 <= slot < L, n >= 1 and t0 + n <= T; d may be any value with d * element
+ * size a multiple of 16 bytes; other errors as for moda_fwd.
+ */
+moda_status_t moda_depth_append(const moda_problem_t* p, const void* layer, int64_t slot,
+                                int64_t t0, int64_t n, void* packed, void* stream);
+
+/*
  * Depth-KV layout packer: layer-major depth entries layers[L, B, Hk, T, d]
  * (entry l of every token contiguous, the natural per-layer layout whose
  * stride between a token's layers defeats coalescing) to the token-major

@@ -172,3 +172,28 @@ def test_timing_hook_argument_checks():
     assert lib.moda_timing_count() == 0
     assert lib.moda_timing_label(0) is None
     assert lib.moda_timing_label(-1) is None
+
+
+def test_decode_and_append_argument_checks():
+    lib = mb.load()
+    p = prob(T=16, L=2)
+    ws = 0x20000
+    need = mb.moda_decode_workspace_bytes(p)
+    assert need > 0 and need % 256 == 0
+    assert mb.moda_decode_workspace_bytes(prob(dtype=mb.MODA_F32)) == 0
+    dec = lambda pp, pos, wsb=1 << 30, q=A: lib.moda_decode(  # noqa: E731
+        ctypes.byref(pp), pos, q, A, A, A, A, A, A, ws, wsb, None)
+    assert dec(p, -1) == mb.MODA_ERR_INVALID_ARGUMENT
+    assert dec(p, 16) == mb.MODA_ERR_INVALID_ARGUMENT
+    assert dec(p, 3, wsb=need - 1) == mb.MODA_ERR_INVALID_ARGUMENT
+    assert dec(p, 3, q=MIS) == mb.MODA_ERR_INVALID_ARGUMENT
+    assert dec(prob(T=16, L=2, dtype=mb.MODA_F32), 3) == mb.MODA_ERR_UNSUPPORTED
+    app = lambda pp, slot, t0, n, layer=A: lib.moda_depth_append(  # noqa: E731
+        ctypes.byref(pp), layer, slot, t0, n, A, None)
+    assert app(p, -1, 0, 1) == mb.MODA_ERR_INVALID_ARGUMENT
+    assert app(p, 2, 0, 1) == mb.MODA_ERR_INVALID_ARGUMENT
+    assert app(p, 1, 10, 7) == mb.MODA_ERR_INVALID_ARGUMENT
+    assert app(p, 1, 0, 0) == mb.MODA_ERR_INVALID_ARGUMENT
+    assert app(prob(L=0), 0, 0, 1) == mb.MODA_ERR_INVALID_ARGUMENT
+    assert app(p, 1, 0, 1, layer=None) == mb.MODA_ERR_INVALID_ARGUMENT
+    assert app(prob(d=4, dtype=mb.MODA_BF16), 0, 0, 1) == mb.MODA_ERR_UNSUPPORTED

@@ -28,7 +28,7 @@ MODA_NOALLOC_SCRATCH_BYTES = 256 << 20
 _TORCH_DTYPE = {MODA_BF16: torch.bfloat16, MODA_F32: torch.float32}
 
 EXPORTS = ("moda_fwd", "moda_bwd", "moda_bwd_workspace_bytes", "moda_bwd_noalloc",
-           "moda_pack_depth",
+           "moda_decode", "moda_decode_workspace_bytes", "moda_depth_append", "moda_pack_depth",
            "moda_status_string", "moda_last_error", "moda_fwd_chunk_tokens", "moda_timing_arm",
            "moda_timing_count", "moda_timing_label")
 
@@ -66,6 +66,13 @@ def load(path: str = LIB_PATH):
         lib.moda_bwd_noalloc.restype = I
         lib.moda_bwd_workspace_bytes.argtypes = [PP]
         lib.moda_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.moda_decode_workspace_bytes.argtypes = [PP]
+        lib.moda_decode_workspace_bytes.restype = ctypes.c_size_t
+        lib.moda_decode.argtypes = [PP, ctypes.c_int64] + [P] * 8 + [ctypes.c_size_t, P]
+        lib.moda_decode.restype = I
+        lib.moda_depth_append.argtypes = [PP, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                          P, P]
+        lib.moda_depth_append.restype = I
         lib.moda_pack_depth.argtypes = [PP, P, P, P]
         lib.moda_pack_depth.restype = I
         lib.moda_status_string.argtypes = [I]
@@ -138,6 +145,19 @@ def _check_tensors(specs):
         dev = t.device
 
 
+def _workspace_bytes(workspace, workspace_bytes):
+    """Usable bytes of a workspace tensor (never more than it holds), or the given count
+    for a raw pointer."""
+    if isinstance(workspace, torch.Tensor):
+        if not workspace.is_contiguous() or workspace.device.type != "cuda":
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        nbytes = workspace.numel() * workspace.element_size()
+        return nbytes if workspace_bytes is None else min(int(workspace_bytes), nbytes)
+    if workspace_bytes is None:
+        raise ValueError("workspace_bytes is required with a raw workspace pointer")
+    return int(workspace_bytes)
+
+
 def _shapes(p: Problem):
     q = (p.B, p.Hq, p.T, p.d)
     kv = (p.B, p.Hk, p.T, p.d)
@@ -193,14 +213,7 @@ def moda_bwd(p: Problem, Q, K, V, Kd, Vd, O, lse, dO, dQ, dK, dV, dKd, dVd, work
                         ("O", O, q, dt), ("lse", lse, rows, torch.float32), ("dO", dO, q, dt),
                         ("dQ", dQ, q, dt), ("dK", dK, kv, dt), ("dV", dV, kv, dt),
                         ("dKd", dKd, dep, dt, nodep), ("dVd", dVd, dep, dt, nodep)])
-    if isinstance(workspace, torch.Tensor):
-        if not workspace.is_contiguous() or workspace.device.type != "cuda":
-            raise ValueError("workspace must be a contiguous GPU tensor")
-        nbytes = workspace.numel() * workspace.element_size()
-        if workspace_bytes is None or workspace_bytes > nbytes:
-            workspace_bytes = nbytes
-    elif workspace_bytes is None:
-        raise ValueError("workspace_bytes is required with a raw workspace pointer")
+    workspace_bytes = _workspace_bytes(workspace, workspace_bytes)
     _check(load().moda_bwd(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Kd), _ptr(Vd),
                            _ptr(O), _ptr(lse), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV),
                            _ptr(dKd), _ptr(dVd), _ptr(workspace), int(workspace_bytes),
@@ -231,6 +244,40 @@ def moda_pack_depth(p: Problem, layers, packed, stream=None) -> None:
         _check_tensors([("layers", layers, (p.L, p.B, p.Hk, p.T, p.d), dt),
                         ("packed", packed, (p.B, p.Hk, p.T * p.L, p.d), dt)])
     _check(load().moda_pack_depth(ctypes.byref(p), _ptr(layers), _ptr(packed), _stream(stream)))
+
+
+def moda_decode_workspace_bytes(p: Problem) -> int:
+    return int(load().moda_decode_workspace_bytes(ctypes.byref(p)))
+
+
+def moda_decode(p: Problem, pos: int, q, K, V, Kd, Vd, O, lse, workspace, workspace_bytes=None,
+                stream=None) -> None:
+    """One new query token at cache position pos: q, O [B,Hq,d]; lse [B,Hq]; K, V
+    [B,Hk,T,d] and Kd, Vd [B,Hk,T*L,d] caches of T tokens."""
+    dt = _TORCH_DTYPE.get(p.dtype)
+    if dt is not None:
+        _, kv, dep, _ = _shapes(p)
+        nodep = p.L == 0
+        _check_tensors([("q", q, (p.B, p.Hq, p.d), dt), ("K", K, kv, dt), ("V", V, kv, dt),
+                        ("Kd", Kd, dep, dt, nodep), ("Vd", Vd, dep, dt, nodep),
+                        ("O", O, (p.B, p.Hq, p.d), dt), ("lse", lse, (p.B, p.Hq), torch.float32)])
+    workspace_bytes = _workspace_bytes(workspace, workspace_bytes)
+    _check(load().moda_decode(ctypes.byref(p), int(pos), _ptr(q), _ptr(K), _ptr(V), _ptr(Kd),
+                              _ptr(Vd), _ptr(O), _ptr(lse), _ptr(workspace), int(workspace_bytes),
+                              _stream(stream)))
+
+
+def moda_depth_append(p: Problem, layer, slot: int, t0: int, packed, stream=None) -> None:
+    """Write layer [B,Hk,n,d] (tokens t0..t0+n-1) into slot `slot` of packed [B,Hk,T*L,d]."""
+    dt = _TORCH_DTYPE.get(p.dtype)
+    n = layer.shape[2] if isinstance(layer, torch.Tensor) and layer.dim() == 4 else None
+    if n is None:
+        raise ValueError("layer must be a [B,Hk,n,d] tensor")
+    if dt is not None:
+        _check_tensors([("layer", layer, (p.B, p.Hk, n, p.d), dt),
+                        ("packed", packed, (p.B, p.Hk, p.T * p.L, p.d), dt)])
+    _check(load().moda_depth_append(ctypes.byref(p), _ptr(layer), int(slot), int(t0), int(n),
+                                    _ptr(packed), _stream(stream)))
 
 
 def moda_fwd_chunk_tokens(p: Problem) -> int:
@@ -321,3 +368,32 @@ def pack_depth(layers, stream=None):
     out = torch.empty((B, Hk, T * L, d), device=layers.device, dtype=layers.dtype)
     moda_pack_depth(p, layers, out, stream)
     return out
+
+
+def decode(q, K, V, Kd, Vd, L, pos, scale=None, window=0, causal=True, stream=None):
+    """(O [B,Hq,d], lse [B,Hq]) of one new token at cache position pos."""
+    B, Hq, d = q.shape
+    Hk, T = K.shape[1], K.shape[2]
+    dt = {torch.bfloat16: MODA_BF16, torch.float32: MODA_F32}.get(q.dtype)
+    if dt is None:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    p = problem(B, Hq, Hk, T, d, L, scale, dt, 0, 0 if causal else MODA_NONCAUSAL, window)
+    O = torch.empty_like(q)
+    lse = torch.empty((B, Hq), device=q.device, dtype=torch.float32)
+    ws = torch.empty(max(moda_decode_workspace_bytes(p), 256), device=q.device,
+                     dtype=torch.uint8)
+    moda_decode(p, pos, q, K, V, Kd, Vd, O, lse, ws, stream=stream)
+    return O, lse
+
+
+def depth_append(packed, layer, L, slot, t0=0, stream=None):
+    """Write layer [B,Hk,n,d] into slot `slot` of packed [B,Hk,T*L,d] in place."""
+    B, Hk, TL, d = packed.shape
+    if TL % L:
+        raise ValueError("packed rows are not a multiple of L")
+    dt = {torch.bfloat16: MODA_BF16, torch.float32: MODA_F32}.get(packed.dtype)
+    if dt is None:
+        raise TypeError(f"unsupported dtype {packed.dtype}")
+    p = problem(B, Hk, Hk, TL // L, d, L, 1.0, dt)
+    moda_depth_append(p, layer, slot, t0, packed, stream)
+    return packed

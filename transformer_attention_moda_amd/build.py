@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoda.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "rowwise.hip", "pack.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "decode.hip", "rowwise.hip", "pack.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]

@@ -362,6 +362,68 @@ moda_status_t moda_bwd_noalloc(const moda_problem_t* p, const void* Q, const voi
     return launch_bwd(p, s, Q, K, V, Kd, Vd, O, lse, dO, dQ, dK, dV, dKd, dVd, ws, hs);
 }
 
+size_t moda_decode_workspace_bytes(const moda_problem_t* p)
+{
+    moda::Shape s;
+    if (check_problem(p, true, &s) != MODA_OK || p->dtype != MODA_BF16) return 0;
+    // The split grows with the number of visible keys: the whole cache bounds it.
+    return moda::decode_ws_bytes(moda::plan_decode(s, s.T));
+}
+
+moda_status_t moda_decode(const moda_problem_t* p, int64_t pos, const void* q, const void* K,
+                          const void* V, const void* Kd, const void* Vd, void* O, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream)
+{
+    moda::Shape s;
+    moda_status_t st = check_problem(p, true, &s);
+    if (st != MODA_OK) return st;
+    if (p->dtype != MODA_BF16)
+        return fail(MODA_ERR_UNSUPPORTED, "moda_decode is built for MODA_BF16 only");
+    if (pos < 0 || pos >= p->T)
+        return fail(MODA_ERR_INVALID_ARGUMENT, "pos = %lld outside the cache of T = %lld tokens",
+                    (long long)pos, (long long)p->T);
+    const void* ptrs[] = {q, K, V, O, lse};
+    const char* names[] = {"q", "K", "V", "O", "lse"};
+    for (int i = 0; i < 5; ++i)
+        if ((st = check_ptr(ptrs[i], names[i])) != MODA_OK) return st;
+    if ((st = check_depth(p, Kd, "Kd", Vd, "Vd")) != MODA_OK) return st;
+    if (!workspace) return fail(MODA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(MODA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    const size_t need = moda::decode_ws_bytes(moda::plan_decode(s, s.noncausal ? s.T : pos + 1));
+    if (workspace_bytes < need)
+        return fail(MODA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu required",
+                    workspace_bytes, need);
+    return hip_status(moda::launch_decode_bf16(s, pos, q, K, V, Kd, Vd, O, lse, workspace,
+                                               reinterpret_cast<hipStream_t>(stream)),
+                      "moda_decode launch");
+}
+
+moda_status_t moda_depth_append(const moda_problem_t* p, const void* layer, int64_t slot,
+                                int64_t t0, int64_t n, void* packed, void* stream)
+{
+    moda::Shape s;
+    moda_status_t st = check_problem(p, false, &s);
+    if (st != MODA_OK) return st;
+    if (p->L < 1) return fail(MODA_ERR_INVALID_ARGUMENT, "moda_depth_append needs L >= 1");
+    if (slot < 0 || slot >= p->L)
+        return fail(MODA_ERR_INVALID_ARGUMENT, "slot %lld outside 0..L-1 (L = %lld)",
+                    (long long)slot, (long long)p->L);
+    if (n < 1 || t0 < 0 || t0 > p->T - n)
+        return fail(MODA_ERR_INVALID_ARGUMENT, "tokens %lld..%lld outside the cache of T = %lld",
+                    (long long)t0, (long long)(t0 + n - 1), (long long)p->T);
+    const int64_t row_bytes = p->d * elem_size(p->dtype);
+    if (row_bytes % 16 != 0)
+        return fail(MODA_ERR_UNSUPPORTED, "row of %lld bytes is not a multiple of 16",
+                    (long long)row_bytes);
+    if ((st = check_ptr(layer, "layer")) != MODA_OK) return st;
+    if ((st = check_ptr(packed, "packed")) != MODA_OK) return st;
+    return hip_status(moda::launch_depth_append(p->B, p->Hk, p->T, p->L, row_bytes, slot, t0, n,
+                                                layer, packed,
+                                                reinterpret_cast<hipStream_t>(stream)),
+                      "moda_depth_append launch");
+}
+
 moda_status_t moda_pack_depth(const moda_problem_t* p, const void* layers, void* packed,
                               void* stream)
 {

@@ -59,51 +59,6 @@ struct FwdArgs {
 
 constexpr int BN = 64;  // keys per sequence tile
 
-// Sequence tiles beyond this threshold of max growth (log2 units) trigger a
-// rescale of the running output and sum; below it the stale max is kept and the
-// weights stay below 2^8, exactly representable in the same way.
-constexpr float kRescaleLog2 = 8.f;
-
-// Online-softmax update of one lane's column with the scores held in s[0..NB-1]
-// (raw q.k values, 16 per block; masked entries are -inf).  The running max m
-// is raised (and o, l rescaled by 2^(c(m - m_new))) only when some lane of the
-// wave would otherwise see a weight above 2^kRescaleLog2; o/l = softmax output
-// holds for any m, so keeping a stale m is exact.  On return s holds the
-// weights exp2(c*(score - m)).
-template <int D, int NB, bool SUM = true>
-__device__ __forceinline__ void softmax_update(f32x16 (&s)[2], float& m, float& l,
-                                               f32x16 (&o)[D / 32], float c)
-{
-    float mt = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mt = fmaxf(mt, s[kb][j]);
-    mt = max_halves(mt);
-    const bool grow = (mt - m) * c > kRescaleLog2;   // true for the first visible score
-    if (__any(grow)) {
-        const float m_new = fmaxf(m, mt);
-        const float alpha = fast_exp2((m - m_new) * c);
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
-        m = m_new;
-    }
-    const float mc = m * c;
-    float ps = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const float p = fast_exp2(fmaf(s[kb][j], c, -mc));
-            s[kb][j] = p;
-            ps += p;
-        }
-    if (SUM) l += sum_halves(ps);
-}
-
 // Adds the 8 bf16 values of p to acc (packed dot products with 1): the row sum of
 // exactly the weights the PV product consumes, at half the instructions of fp32 adds.
 __device__ __forceinline__ float row_sum_bf16(const bf16x8& p, float acc)

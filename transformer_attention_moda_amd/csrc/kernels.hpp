@@ -38,6 +38,25 @@ hipError_t launch_bwd_f32(const Shape& s, const float* Q, const float* K, const 
                           const float* dO, float* dQ, float* dK, float* dV, float* dKd,
                           float* dVd, float* ws, hipStream_t st);
 
+// Decoding step (bfloat16): how the visible keys of one query token are split into
+// partials, and the launch.  nseq: visible sequence keys.
+struct DecodePlan {
+    int64_t nblk_seq, nblk;   // 32-row blocks: sequence, then depth
+    int64_t nsplit, bpw;      // workgroups per (b, kv); blocks per wave
+    int64_t o_floats, ml_floats;
+};
+DecodePlan plan_decode(const Shape& s, int64_t nseq);
+size_t decode_ws_bytes(const DecodePlan& pl);
+hipError_t launch_decode_bf16(const Shape& s, int64_t pos, const void* q, const void* K,
+                              const void* V, const void* Kd, const void* Vd, void* O, float* lse,
+                              void* ws, hipStream_t st);
+
+// Depth-cache append: layer [B, Hk, n, row_bytes] -> rows (t0+i)*L + slot of
+// packed [B, Hk, T*L, row_bytes].
+hipError_t launch_depth_append(int64_t B, int64_t Hk, int64_t T, int64_t L, int64_t row_bytes,
+                               int64_t slot, int64_t t0, int64_t n, const void* layer,
+                               void* packed, hipStream_t st);
+
 // Depth packer: [L, B, Hk, T, row_bytes] -> [B, Hk, T*L, row_bytes].
 hipError_t launch_pack_depth(int64_t L, int64_t B, int64_t Hk, int64_t T, int64_t row_bytes,
                              const void* layers, void* packed, hipStream_t st);

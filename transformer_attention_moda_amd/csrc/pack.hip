@@ -1,5 +1,8 @@
 // Depth-KV layout packer: layer-major [L, B, Hk, T, d] -> token-major
-// [B, Hk, T*L, d], packed row t*L + l = layers[l, b, kv, t].
+// [B, Hk, T*L, d], packed row t*L + l = layers[l, b, kv, t]; and its
+// append form, one layer's entries for a token range written into one slot of
+// an existing packed cache (the DepthKVCache role of the "moda-attention 0.1.0"
+// PyPI page's architecture list: contiguous depth KV storage across layers).
 //
 // In the natural per-layer layout the L entries of one token lie T*d elements
 // apart, which defeats coalesced reads in the attention kernel; the flattened
@@ -44,7 +47,39 @@ __global__ __launch_bounds__(PACK_THREADS) void pack_kernel(const u32x4* __restr
     }
 }
 
+// Append: chunk i of the [B*Hk*n, cpr] source rows goes to chunk i % cpr of depth row
+// (t0 + r % n)*L + slot of block r / n, r = i / cpr.
+__global__ __launch_bounds__(PACK_THREADS) void append_kernel(const u32x4* __restrict__ in,
+                                                              u32x4* __restrict__ out,
+                                                              int64_t chunks, int64_t cpr,
+                                                              int64_t n, int64_t T, int64_t L,
+                                                              int64_t t0, int64_t slot)
+{
+    for (int64_t i = (int64_t)blockIdx.x * PACK_THREADS + threadIdx.x; i < chunks;
+         i += (int64_t)gridDim.x * PACK_THREADS) {
+        const int64_t r = i / cpr, ch = i - r * cpr;
+        const int64_t bkv = r / n, t = t0 + (r - bkv * n);
+        __builtin_nontemporal_store(__builtin_nontemporal_load(in + i),
+                                    out + ((bkv * T + t) * L + slot) * cpr + ch);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_depth_append(int64_t B, int64_t Hk, int64_t T, int64_t L, int64_t row_bytes,
+                               int64_t slot, int64_t t0, int64_t n, const void* layer,
+                               void* packed, hipStream_t st)
+{
+    const int64_t cpr = row_bytes / 16;
+    const int64_t chunks = B * Hk * n * cpr;
+    int64_t blocks = (chunks + PACK_THREADS - 1) / PACK_THREADS;
+    if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
+    timing_begin("depth_append", st);
+    hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(PACK_THREADS), 0, st,
+                       (const u32x4*)layer, (u32x4*)packed, chunks, cpr, n, T, L, t0, slot);
+    timing_end(st);
+    return hipGetLastError();
+}
 
 hipError_t launch_pack_depth(int64_t L, int64_t B, int64_t Hk, int64_t T, int64_t row_bytes,
                              const void* layers, void* packed, hipStream_t st)
