@@ -10,7 +10,15 @@ sequence (B=1, Hq=16, Hk=8, T=65536, d=128, L=24, bf16).
 Printed: one JSON line.  `value` is algorithmic forward+backward TFLOP/s of
 the whole step (forward FLOP = 4 d B Hq (T(T+1)/2 + T L), backward = 2.5x
 forward); the same step with L=0 (no depth: plain causal attention through
-the same entry points) gives the overhead of the depth path.
+the same entry points) gives the overhead of the depth path.  `aux` adds the
+1.5B-like layer's forward overhead against its L=0 path, cold-cache HBM rates of
+the small-model forward and the training-shape forward+backward, and the depth
+utilisation of the tiling.
+
+`--suite pages` prints one JSON line per kernel workload of the pages' efficiency
+tables (sequence, group and depth sweeps at d=64) and per depth-scan ablation
+mode; `--suite decode` one line each for the decoding step, the depth-cache
+append and the non-causal and windowed variants at the 64K shape.
 """
 from __future__ import annotations
 
@@ -39,6 +47,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_64k")
+    ap.add_argument("--suite", choices=["pages", "decode"], default=None,
+                    help="print one JSON line per workload of a measurement suite instead")
+    ap.add_argument("--no-aux", action="store_true", help="skip the auxiliary measurements")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -50,41 +61,58 @@ def parse():
 
 
 class Step:
-    """Buffers and the launches of one step, with per-entry-point events."""
+    """Buffers and the launches of one step, with per-entry-point events.  pack: the
+    step starts by packing layer-major depth K and V (else the packed depth rows are
+    drawn directly); bwd: the step includes the backward."""
 
-    def __init__(self, w, L, seed=0):
+    def __init__(self, w, L, seed=0, pack=True, bwd=True, causal=True, window=0):
         import torch
         from transformer_attention_moda_amd import binding, inputs
         self.torch, self.mb, self.w, self.L = torch, binding, w, L
+        self.pack, self.bwd = pack and L > 0, bwd
         dev = "cuda:0"
-        names = ["Q", "K", "V", "dO"] + (["layers_K", "layers_V"] if L > 0 else [])
+        names = ["Q", "K", "V"] + (["dO"] if bwd else [])
+        if L > 0:
+            names += ["layers_K", "layers_V"] if self.pack else ["Kd", "Vd"]
         x = inputs.make(w.with_(L=L), seed=seed, device=dev, names=names)
         self.x = x
-        self.p = binding.problem_for(x["Q"], x["K"], L, w.scale, chunk=0)
+        self.p = binding.problem_for(x["Q"], x["K"], L, w.scale, chunk=0, causal=causal,
+                                     window=window)
         B, Hk, T, d = w.B, w.Hk, w.T, w.d
         empty = lambda shape: torch.empty(shape, device=dev, dtype=torch.bfloat16)  # noqa: E731
-        self.Kd = empty((B, Hk, T * L, d)) if L > 0 else None
-        self.Vd = empty((B, Hk, T * L, d)) if L > 0 else None
+        if self.pack:
+            self.Kd = empty((B, Hk, T * L, d))
+            self.Vd = empty((B, Hk, T * L, d))
+        else:
+            self.Kd, self.Vd = x.get("Kd"), x.get("Vd")
         self.O = torch.empty_like(x["Q"])
         self.lse = torch.empty((w.B, w.Hq, T), device=dev, dtype=torch.float32)
-        self.dQ, self.dK, self.dV = (torch.empty_like(x["Q"]), torch.empty_like(x["K"]),
-                                     torch.empty_like(x["V"]))
-        self.dKd = torch.empty_like(self.Kd) if L > 0 else None
-        self.dVd = torch.empty_like(self.Vd) if L > 0 else None
-        nws = binding.moda_bwd_workspace_bytes(self.p)
-        self.ws = torch.empty(max(nws, 256), device=dev, dtype=torch.uint8)
-        if L > 0:
+        if bwd:
+            self.dQ, self.dK, self.dV = (torch.empty_like(x["Q"]), torch.empty_like(x["K"]),
+                                         torch.empty_like(x["V"]))
+            self.dKd = torch.empty_like(self.Kd) if L > 0 else None
+            self.dVd = torch.empty_like(self.Vd) if L > 0 else None
+            nws = binding.moda_bwd_workspace_bytes(self.p)
+            self.ws = torch.empty(max(nws, 256), device=dev, dtype=torch.uint8)
+        if self.pack:
             self.pp = binding.problem(B, Hk, Hk, T, d, L, 1.0, binding.MODA_BF16)
         self.events = []
 
     def run(self):
         mb, x = self.mb, self.x
-        if self.L > 0:
+        if self.pack:
             mb.moda_pack_depth(self.pp, x["layers_K"], self.Kd)
             mb.moda_pack_depth(self.pp, x["layers_V"], self.Vd)
         mb.moda_fwd(self.p, x["Q"], x["K"], x["V"], self.Kd, self.Vd, self.O, self.lse)
-        mb.moda_bwd(self.p, x["Q"], x["K"], x["V"], self.Kd, self.Vd, self.O, self.lse, x["dO"],
-                    self.dQ, self.dK, self.dV, self.dKd, self.dVd, self.ws)
+        if self.bwd:
+            mb.moda_bwd(self.p, x["Q"], x["K"], x["V"], self.Kd, self.Vd, self.O, self.lse,
+                        x["dO"], self.dQ, self.dK, self.dV, self.dKd, self.dVd, self.ws)
+
+    def free(self):
+        for k in list(vars(self)):
+            if k not in ("torch", "mb", "w", "L", "p"):
+                delattr(self, k)
+        self.torch.cuda.empty_cache()
 
     def timed(self, steps, warmup):
         """Average step time (ms) over `steps`, and per kernel the average
@@ -233,11 +261,265 @@ def cpu_baseline(w, step, seconds):
     dt, fl, t_lo = sample(n)
     return {
         "value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": th, "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": (f"fp64 forward+backward of tokens {t_lo}..{T - 1} of one KV group "
                    f"({G} query heads, b=0, kv=0) of the {w.name} workload; "
                    f"{dt:.1f} s on {th} threads; algorithmic FLOP of the sample "
                    f"(3.5 x 4 d x visible pairs) / wall time"),
     }
+
+
+def cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def depth_eta(w, scan=0, window=0, rows_per_wg=256):
+    """Depth utilisation of the forward's tiling: the fraction of the depth scores it
+    computes that the mask keeps (the "Depth Utilization" of the pages' efficiency tables).
+    Each 32-row query block (one wave) scores 32x32 MFMA blocks of depth rows: of its own
+    tokens (scan 0), of its workgroup chunk's (1), or all of the KV head's (2); every
+    query sees exactly W of them."""
+    G, T, L = w.G, w.T, w.L
+    W = window if window else L
+    if L == 0:
+        return None
+    TG = T * G
+    computed = 0
+    for c in range((TG + rows_per_wg - 1) // rows_per_wg):
+        r0 = c * rows_per_wg
+        for wv in range(rows_per_wg // 32):
+            fw = r0 + 32 * wv
+            if scan == 0:
+                first, last = min(fw // G, T - 1), min((fw + 31) // G, T - 1)
+            elif scan == 1:
+                first, last = min(r0 // G, T - 1), min((r0 + rows_per_wg - 1) // G, T - 1)
+            else:
+                first, last = 0, T - 1
+            computed += -(-((last - first + 1) * W) // 32) * 32 * 32
+    return w.Hq * T * W / (w.Hk * computed)
+
+
+def fwd_bytes(w, L=None, W=None):
+    """Bytes the forward must move once: Q read, O written, K, V and the visible depth
+    rows read, lse written."""
+    L = w.L if L is None else L
+    W = L if W is None else W
+    eb = 2
+    return (eb * (2 * w.B * w.Hq * w.T * w.d + 2 * w.B * w.Hk * w.T * w.d
+                  + 2 * w.B * w.Hk * w.T * W * w.d) + 4 * w.B * w.Hq * w.T)
+
+
+def bwd_bytes(w):
+    """Bytes the backward must move once: Q, O, dO read and dQ written; K, V read and dK,
+    dV written; the depth rows read and their gradients written; lse read."""
+    eb = 2
+    return (eb * (4 * w.B * w.Hq * w.T * w.d + 4 * w.B * w.Hk * w.T * w.d
+                  + 4 * w.B * w.Hk * w.T * w.L * w.d) + 4 * w.B * w.Hq * w.T)
+
+
+def events_ms(torch, fn, reps, flush=None):
+    """Median milliseconds of fn() over reps runs, timed with events on the current
+    stream; flush() (untimed) runs before each."""
+    out = []
+    for _ in range(reps):
+        if flush:
+            flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1))
+    out.sort()
+    return out[len(out) // 2]
+
+
+def cold_rates(torch, inputs):
+    """HBM rate with cold caches: before each timed run a 1 GiB buffer is written, which
+    evicts the 256 MB last-level cache and the L2s.  The small-model forward and the
+    training-shape forward+backward, each against the bytes it must move once."""
+    flush_buf = torch.empty(1 << 30, device="cuda:0", dtype=torch.uint8)
+    flush = lambda: flush_buf.fill_(1)  # noqa: E731
+    out = {}
+    for name, with_bwd in (("small_model", False), ("train_4k", True)):
+        w = inputs.WORKLOADS[name]
+        st = Step(w, w.L, seed=0, pack=False, bwd=with_bwd)
+        st.run()
+        ms = events_ms(torch, st.run, 9, flush)
+        nbytes = fwd_bytes(w) + (bwd_bytes(w) if with_bwd else 0)
+        out[f"{name}_cold"] = {"what": "forward+backward" if with_bwd else "forward",
+                               "ms": round(ms, 4), "bytes": nbytes,
+                               "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                               "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        st.free()
+    del flush_buf
+    torch.cuda.empty_cache()
+    return out
+
+
+def fwd_pair(torch, w, reps=9, **kw):
+    """Median forward milliseconds of w at its L and at L = 0, launched alternately."""
+    a = Step(w, w.L, seed=0, pack=False, bwd=False, **kw)
+    b = Step(w, 0, seed=0, pack=False, bwd=False)
+    a.run()
+    b.run()
+    ta, tb = [], []
+    for _ in range(reps):
+        ta.append(events_ms(torch, a.run, 1))
+        tb.append(events_ms(torch, b.run, 1))
+    a.free()
+    b.free()
+    ta.sort()
+    tb.sort()
+    return ta[reps // 2], tb[reps // 2]
+
+
+def aux_measurements(torch, inputs):
+    w = inputs.WORKLOADS["layer_1p5b_8k"]
+    fl, f0 = fwd_pair(torch, w)
+    out = {"layer_1p5b_8k": {
+        "fwd_ms": round(fl, 4), "fwd_ms_L0": round(f0, 4),
+        "fwd_tflops": round(fwd_flops(w) / (fl * 1e-3) / 1e12, 1),
+        "overhead_fwd": round((fl - f0) / f0, 4),
+        "overhead_fwd_pages_convention": round((fl - f0) / fl, 4),
+        "eta": round(depth_eta(w), 4)}}
+    out.update(cold_rates(torch, inputs))
+    return out
+
+
+# The pages' own figures for the workloads of --suite pages (README "Kernel Efficiency"
+# tables: A100, bf16, forward+backward, FlashAttention-2 vs MoDA Triton kernels, in ms, and
+# the extra time they print).  Context only: other hardware and other kernels.
+PAGES_A100 = {
+    "table2_T4096": (7.970, 10.750, 0.2586), "table2_T8192": (28.700, 35.427, 0.1899),
+    "table2_T16384": (116.700, 127.661, 0.0859), "table2_T32768": (459.854, 480.914, 0.0438),
+    "table2_T65536": (1831.668, 1883.026, 0.0273), "table2_G2": (28.982, 39.741, 0.2707),
+    "table2_G4": (58.071, 68.939, 0.1576), "table2_G16": (233.700, 244.900, 0.0457),
+    "table2_G32": (467.107, 480.767, 0.0284), "table2_L128": (116.700, 138.224, 0.1557),
+    "table2_L256": (116.700, 167.958, 0.3052),
+}
+
+
+def suite_pages(torch, inputs, steps, warmup):
+    """One line per workload of the pages' efficiency tables: forward+backward at L and at
+    L = 0 through the same entry points (depth rows already packed), and the depth-scan
+    ablation at the Table 7 shape."""
+    for name, w in inputs.PAGE_WORKLOADS.items():
+        st = Step(w, w.L, seed=0, pack=False)
+        ms, k, _ = st.timed(steps, warmup)
+        st.free()
+        s0 = Step(w, 0, seed=0, pack=False)
+        ms0, k0, _ = s0.timed(steps, warmup)
+        s0.free()
+        fl = 3.5 * fwd_flops(w)
+        fwd, fwd0 = k["fwd"]["avg_ms"], k0["fwd"]["avg_ms"]
+        line = {
+            "metric": "MoDA fwd+bwd TFLOP/s bf16 (pages' kernel workload)",
+            "value": round(fl / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hk": w.Hk, "T": w.T, "d": w.d,
+                       "L": w.L, "G": w.G},
+            "ms": round(ms, 4), "ms_L0": round(ms0, 4), "fwd_ms": round(fwd, 4),
+            "fwd_ms_L0": round(fwd0, 4),
+            "fwd_tflops": round(fwd_flops(w) / (fwd * 1e-3) / 1e12, 2),
+            "frac_mfma_fwd_bwd": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "overhead_fwd_bwd": round((ms - ms0) / ms0, 4),
+            "overhead_fwd_bwd_pages_convention": round((ms - ms0) / ms, 4),
+            "overhead_fwd": round((fwd - fwd0) / fwd0, 4),
+            "eta": round(depth_eta(w), 4),
+            "kernels_ms": {n: round(v["avg_ms"], 4) for n, v in k.items()},
+        }
+        if name in PAGES_A100:
+            fa2, moda, extra = PAGES_A100[name]
+            line["pages_a100_context"] = {"fa2_ms": fa2, "moda_ms": moda, "extra_time": extra}
+        print(json.dumps(line), flush=True)
+    w = inputs.PAGE_WORKLOADS["table7"]
+    st = Step(w, w.L, seed=0, pack=False, bwd=False)
+    mb, x = st.mb, st.x
+    labels = {0: "own tokens per query block (library)", 1: "whole query chunk (chunk-aware)",
+              2: "all T*L rows (flat layout, no chunking)"}
+    for scan in (0, 1, 2):
+        run = lambda: mb.moda_fwd_depth_scan(st.p, scan, x["Q"], x["K"], x["V"], st.Kd,  # noqa: E731
+                                             st.Vd, st.O, st.lse)
+        run()
+        ms = events_ms(torch, run, 9)
+        eta = depth_eta(w, scan)
+        print(json.dumps({
+            "metric": "MoDA forward ms, depth-scan ablation (Table 7 shape)", "value": round(ms, 4),
+            "unit": "ms", "config": {"workload": "table7", "scan": scan, "layout": labels[scan]},
+            "eta": round(eta, 6),
+            # K and V rows of d bf16 scored once per 32x32 block of (rows, queries)
+            "depth_bytes_read_GB": round(4 * w.d * w.B * w.Hq * w.T * w.L / (32 * eta) / 1e9, 3),
+            "pages_table7_context_ms": {0: 1.460, 1: 6.286, 2: 13.102}[scan]}), flush=True)
+    st.free()
+
+
+def suite_decode(torch, inputs, steps):
+    """Decode, depth append and the variants at the 64K shape (B=1, Hq=16, Hk=8, d=128,
+    L=24), each against its roofline."""
+    from transformer_attention_moda_amd import binding as mb
+    w = inputs.WORKLOADS["long_64k"]
+    for B, window in ((1, 0), (16, 0), (1, 4)):
+        wb = w.with_(B=B)
+        x = inputs.make(wb, seed=0, device="cuda:0", names=("Q", "K", "V", "Kd", "Vd"))
+        q = x["Q"][:, :, -1].contiguous()
+        p = mb.problem(B, w.Hq, w.Hk, w.T, w.d, w.L, w.scale, window=window)
+        O = torch.empty_like(q)
+        lse = torch.empty((B, w.Hq), device="cuda:0")
+        ws = torch.empty(mb.moda_decode_workspace_bytes(p), device="cuda:0", dtype=torch.uint8)
+        run = lambda: mb.moda_decode(p, w.T - 1, q, x["K"], x["V"], x["Kd"], x["Vd"], O, lse, ws)  # noqa: E731
+        run()
+        ms = events_ms(torch, run, max(steps, 9))
+        W = window or w.L
+        nbytes = 2 * (2 * B * w.Hk * w.T * w.d + 2 * B * w.Hk * W * w.d + 2 * B * w.Hq * w.d)
+        print(json.dumps({
+            "metric": "MoDA decode step GB/s (one new token, 64K cache)",
+            "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "config": {"workload": "decode_64k", "B": B, "Hq": w.Hq, "Hk": w.Hk, "T": w.T,
+                       "d": w.d, "L": w.L, "window": window},
+            "us": round(ms * 1e3, 2), "bytes": nbytes,
+            "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
+        del x, q, O, lse, ws
+        torch.cuda.empty_cache()
+    layer = inputs.normal((w.B, w.Hk, w.T, w.d), seed=0, tensor="layers_K", device="cuda:0")
+    packed = torch.empty((w.B, w.Hk, w.T * w.L, w.d), device="cuda:0", dtype=torch.bfloat16)
+    p = mb.problem(w.B, w.Hk, w.Hk, w.T, w.d, w.L, 1.0)
+    run = lambda: mb.moda_depth_append(p, layer, 5, 0, packed)  # noqa: E731
+    run()
+    ms = events_ms(torch, run, 9)
+    nbytes = 2 * layer.numel() * 2
+    print(json.dumps({"metric": "MoDA depth-cache append GB/s (one layer, 64K tokens)",
+                      "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                      "config": {"workload": "append_64k", "B": w.B, "Hk": w.Hk, "T": w.T,
+                                 "d": w.d, "L": w.L},
+                      "us": round(ms * 1e3, 2),
+                      "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
+    del layer, packed
+    torch.cuda.empty_cache()
+    st = Step(w, w.L, seed=0, pack=False, causal=False)
+    ms, k, _ = st.timed(max(3, steps // 3), 1)
+    st.free()
+    pairs = w.T * w.T + w.T * w.L
+    fl = 3.5 * 4.0 * w.d * w.B * w.Hq * pairs
+    print(json.dumps({"metric": "MoDA non-causal fwd+bwd TFLOP/s bf16 (64K shape)",
+                      "value": round(fl / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                      "config": {"workload": "long_64k_noncausal"}, "ms": round(ms, 3),
+                      "fwd_ms": round(k["fwd"]["avg_ms"], 3),
+                      "frac_mfma": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}),
+          flush=True)
+    fw4, f0 = fwd_pair(torch, w, reps=5, window=4)
+    print(json.dumps({"metric": "MoDA windowed forward ms (last 4 of 24 depth slots, 64K shape)",
+                      "value": round(fw4, 4), "unit": "ms",
+                      "config": {"workload": "long_64k_window4"}, "fwd_ms_L0": round(f0, 4),
+                      "overhead_fwd": round((fw4 - f0) / f0, 4),
+                      "eta": round(depth_eta(w, window=4), 4)}), flush=True)
+
 
 
 def main():
@@ -251,6 +533,12 @@ def main():
     from transformer_attention_moda_amd import binding, inputs
     binding.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.suite == "pages":
+        suite_pages(torch, inputs, args.steps, args.warmup)
+        return
+    if args.suite == "decode":
+        suite_decode(torch, inputs, args.steps)
+        return
     w = inputs.WORKLOADS[args.workload]
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 20
@@ -299,6 +587,8 @@ def main():
             step.run()
             torch.cuda.synchronize()
         cpu = cpu_baseline(w, step, args.cpu_seconds)
+    step.free()
+    aux = None if args.no_aux else aux_measurements(torch, inputs)
 
     out = {
         "metric": "MoDA fwd+bwd TFLOP/s bf16 at T=64K (% MFMA peak); overhead vs own L=0 path",
@@ -316,7 +606,9 @@ def main():
                 "frac": round(f_fwd / (kernels["fwd"]["avg_ms"] * 1e-3) / 1e12 /
                               MFMA_BF16_PEAK_TFLOPS, 4)},
         "kernels": per_kernel,
+        "eta": round(depth_eta(w), 4),
         "cpu_baseline": cpu,
+        "aux": aux,
         "wall_s_timed": round(wall, 3),
     }
     if res0:

@@ -213,6 +213,27 @@ const char* moda_last_error(void);
 int32_t moda_fwd_chunk_tokens(const moda_problem_t* p);
 
 /*
+ * The forward with another choice of the depth rows each 32-row query block
+ * scores (profiling support: an ablation of depth-KV layouts in the manner of
+ * the paper summary's kernel ablation, Table 7 of its experiments section).
+ *   MODA_SCAN_WAVE   its own tokens' rows only: what moda_fwd does (each depth
+ *                    row is scored by the one wave that holds its token's G heads);
+ *   MODA_SCAN_CHUNK  all rows of its workgroup's query chunk (chunk-aware layout);
+ *   MODA_SCAN_ALL    all T*L rows of the KV head (flat layout, no chunking).
+ * The depth matching mask keeps each query's own rows, so O and lse are those of
+ * moda_fwd up to fp32 summation order; only the work and the bytes read grow.
+ * MODA_BF16 only.  Errors as for moda_fwd, plus MODA_ERR_INVALID_ARGUMENT for an
+ * unknown scan.
+ */
+#define MODA_SCAN_WAVE 0
+#define MODA_SCAN_CHUNK 1
+#define MODA_SCAN_ALL 2
+
+moda_status_t moda_fwd_depth_scan(const moda_problem_t* p, int32_t scan, const void* Q,
+                                  const void* K, const void* V, const void* Kd, const void* Vd,
+                                  void* O, float* lse, void* stream);
+
+/*
  * Per-kernel timing hook (profiling support; not part of the operator).
  * events: caller-created hipEvent_t handles (cast to void*), count >= 0.
  * While armed, every kernel a libmoda entry point launches on this thread is

@@ -25,10 +25,12 @@ MODA_BF16, MODA_F32 = 0, 1
 MODA_MAX_L = 1024
 MODA_NONCAUSAL = 1
 MODA_NOALLOC_SCRATCH_BYTES = 256 << 20
+MODA_SCAN_WAVE, MODA_SCAN_CHUNK, MODA_SCAN_ALL = 0, 1, 2
 _TORCH_DTYPE = {MODA_BF16: torch.bfloat16, MODA_F32: torch.float32}
 
 EXPORTS = ("moda_fwd", "moda_bwd", "moda_bwd_workspace_bytes", "moda_bwd_noalloc",
            "moda_decode", "moda_decode_workspace_bytes", "moda_depth_append", "moda_pack_depth",
+           "moda_fwd_depth_scan",
            "moda_status_string", "moda_last_error", "moda_fwd_chunk_tokens", "moda_timing_arm",
            "moda_timing_count", "moda_timing_label")
 
@@ -73,6 +75,8 @@ def load(path: str = LIB_PATH):
         lib.moda_depth_append.argtypes = [PP, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                           P, P]
         lib.moda_depth_append.restype = I
+        lib.moda_fwd_depth_scan.argtypes = [PP, ctypes.c_int32] + [P] * 8
+        lib.moda_fwd_depth_scan.restype = I
         lib.moda_pack_depth.argtypes = [PP, P, P, P]
         lib.moda_pack_depth.restype = I
         lib.moda_status_string.argtypes = [I]
@@ -196,6 +200,19 @@ def moda_fwd(p: Problem, Q, K, V, Kd, Vd, O, lse, stream=None) -> None:
                         ("O", O, q, dt), ("lse", lse, rows, torch.float32)])
     _check(load().moda_fwd(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(Kd), _ptr(Vd),
                            _ptr(O), _ptr(lse), _stream(stream)))
+
+
+def moda_fwd_depth_scan(p: Problem, scan: int, Q, K, V, Kd, Vd, O, lse, stream=None) -> None:
+    """The forward with another depth-row scan (MODA_SCAN_*), for the layout ablation."""
+    dt = _TORCH_DTYPE.get(p.dtype)
+    if dt is not None:
+        q, kv, dep, rows = _shapes(p)
+        nodep = p.L == 0
+        _check_tensors([("Q", Q, q, dt), ("K", K, kv, dt), ("V", V, kv, dt),
+                        ("Kd", Kd, dep, dt, nodep), ("Vd", Vd, dep, dt, nodep),
+                        ("O", O, q, dt), ("lse", lse, rows, torch.float32)])
+    _check(load().moda_fwd_depth_scan(ctypes.byref(p), int(scan), _ptr(Q), _ptr(K), _ptr(V),
+                                      _ptr(Kd), _ptr(Vd), _ptr(O), _ptr(lse), _stream(stream)))
 
 
 def moda_bwd_workspace_bytes(p: Problem) -> int:

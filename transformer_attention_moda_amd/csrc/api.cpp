@@ -315,6 +315,27 @@ moda_status_t moda_fwd(const moda_problem_t* p, const void* Q, const void* K, co
     return hip_status(e, "moda_fwd launch");
 }
 
+moda_status_t moda_fwd_depth_scan(const moda_problem_t* p, int32_t scan, const void* Q,
+                                  const void* K, const void* V, const void* Kd, const void* Vd,
+                                  void* O, float* lse, void* stream)
+{
+    if (scan < MODA_SCAN_WAVE || scan > MODA_SCAN_ALL)
+        return fail(MODA_ERR_INVALID_ARGUMENT, "unknown depth scan %d", (int)scan);
+    moda::Shape s;
+    moda_status_t st = check_problem(p, true, &s);
+    if (st != MODA_OK) return st;
+    if (p->dtype != MODA_BF16)
+        return fail(MODA_ERR_UNSUPPORTED, "the depth-scan ablation is built for MODA_BF16 only");
+    const void* ptrs[] = {Q, K, V, O, lse};
+    const char* names[] = {"Q", "K", "V", "O", "lse"};
+    for (int i = 0; i < 5; ++i)
+        if ((st = check_ptr(ptrs[i], names[i])) != MODA_OK) return st;
+    if ((st = check_depth(p, Kd, "Kd", Vd, "Vd")) != MODA_OK) return st;
+    return hip_status(moda::launch_fwd_bf16(s, Q, K, V, Kd, Vd, O, lse, rows_per_workgroup(p, s.G),
+                                            reinterpret_cast<hipStream_t>(stream), scan),
+                      "moda_fwd_depth_scan launch");
+}
+
 size_t moda_bwd_workspace_bytes(const moda_problem_t* p)
 {
     moda::Shape s;

@@ -52,6 +52,7 @@ struct FwdArgs {
     int Hq, Hk, T, L, G;
     int W;         // visible depth slots per token (the last W of L)
     int noncausal; // every sequence key visible
+    int scan;      // depth rows a wave scores: 0 its tokens', 1 its chunk's, 2 all (ablation)
     int nchunks;   // query chunks per (b, kv)
     float c;       // scale * log2(e)
     float scale;
@@ -149,8 +150,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
         const uint16_t* Kdb = a.Kd + kvbase * (int64_t)L * D;
         const uint16_t* Vdb = a.Vd + kvbase * (int64_t)L * D;
         const int Wn = WIN ? a.W : L;
-        const int64_t dlo = (int64_t)tw_lo * L;
-        const int64_t nv = (int64_t)(tw_hi - tw_lo + 1) * Wn;   // virtual rows of the wave
+        // Tokens whose depth rows the wave scores: its own (the library's layout), or for
+        // the ablation of the depth layouts its workgroup chunk's, or all T; the mask keeps
+        // only the lane's own token, so the result is the same, the work is not.
+        const int t_first = a.scan == 0 ? tw_lo : a.scan == 1 ? (int)min(r0 / G, (int64_t)T - 1) : 0;
+        const int t_last = a.scan == 0 ? tw_hi
+                         : a.scan == 1 ? (int)min((r0 + BM - 1) / G, (int64_t)T - 1) : T - 1;
+        const int64_t dlo = (int64_t)t_first * L;
+        const int64_t nv = (int64_t)(t_last - t_first + 1) * Wn;   // virtual rows of the wave
         const int nblk = (int)((nv + 31) / 32);
         // Depth row of virtual row v (v < nv).
         auto phys = [&](int64_t v) -> int64_t {
@@ -158,7 +165,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
                 return dlo + v;
             } else {
                 const uint32_t vv = (uint32_t)v, tok = vv / (uint32_t)Wn;
-                return (int64_t)(tw_lo + (int)tok) * L + (L - Wn) + (int)(vv - tok * (uint32_t)Wn);
+                return (int64_t)(t_first + (int)tok) * L + (L - Wn) + (int)(vv - tok * (uint32_t)Wn);
             }
         };
         uint16_t* const arr = (w >> 1) == 0 ? lk0 : (w >> 1) == 1 ? lv0 : (w >> 1) == 2 ? lk1 : lv1;
@@ -197,7 +204,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
             for (int si = 0; si < D / 16; ++si) s[0] = mfma32(kr[si], qreg[si], s[0]);
             if (more) issue_k(i + 1);
             // first visible virtual row of this lane's token, relative to the lane's rows
-            const int64_t lo = (int64_t)(tcol - tw_lo) * Wn - 32 * (int64_t)i - 4 * hf;
+            const int64_t lo = (int64_t)(tcol - t_first) * Wn - 32 * (int64_t)i - 4 * hf;
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int rj = (j >> 2) * 8 + (j & 3);
@@ -388,9 +395,10 @@ hipError_t launch(const Shape& s, const FwdArgs& a, int nunits, hipStream_t st)
 
 hipError_t launch_fwd_bf16(const Shape& s, const void* Q, const void* K, const void* V,
                            const void* Kd, const void* Vd, void* O, float* lse, int rows_per_wg,
-                           hipStream_t st)
+                           hipStream_t st, int scan)
 {
     FwdArgs a;
+    a.scan = scan;
     a.Q = (const uint16_t*)Q;
     a.K = (const uint16_t*)K;
     a.V = (const uint16_t*)V;

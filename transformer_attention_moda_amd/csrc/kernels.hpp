@@ -19,10 +19,12 @@ struct Shape {
     int W;           // visible depth slots per token: the last W of L (W == L: all)
 };
 
-// Forward, bfloat16 storage, MFMA.  rows_per_wg is 128 or 256 folded query rows.
+// Forward, bfloat16 storage, MFMA.  rows_per_wg is 128 or 256 folded query rows;
+// scan selects the depth rows a wave scores (0: its own tokens'; 1, 2: the ablation's
+// chunk-wide and all-rows scans).
 hipError_t launch_fwd_bf16(const Shape& s, const void* Q, const void* K, const void* V,
                            const void* Kd, const void* Vd, void* O, float* lse, int rows_per_wg,
-                           hipStream_t st);
+                           hipStream_t st, int scan = 0);
 
 // Backward, bfloat16 storage.  ws: B*Hq*T floats.
 hipError_t launch_bwd_bf16(const Shape& s, const void* Q, const void* K, const void* V,

@@ -67,6 +67,28 @@ WORKLOADS = {
     )
 }
 
+# The kernel workloads of the pages' efficiency tables (README "Kernel Efficiency",
+# bf16, forward and backward, B=1, d=64, Hk=8): the sequence-length sweep (G=8, L=64),
+# the GQA-group sweep (T=16384, L=64, Hq=8G) and the depth sweep (T=16384, G=8), and
+# the kernel-ablation shape of the paper summary's experiments (Table 7: T=1024, G=8,
+# L=64).  The pages' chunk C=64 is their kernel's tiling; these run with this
+# library's default tiling (chunk 0).
+PAGE_WORKLOADS = {
+    w.name: w
+    for w in (
+        [Workload(f"table2_T{T}", B=1, Hq=64, Hk=8, T=T, d=64, L=64, chunk=0, dtype="bf16",
+                  bwd=True) for T in (4096, 8192, 16384, 32768, 65536)]
+        + [Workload(f"table2_G{G}", B=1, Hq=8 * G, Hk=8, T=16384, d=64, L=64, chunk=0,
+                    dtype="bf16", bwd=True) for G in (2, 4, 16, 32)]
+        + [Workload(f"table2_L{L}", B=1, Hq=64, Hk=8, T=16384, d=64, L=L, chunk=0, dtype="bf16",
+                    bwd=True) for L in (128, 256)]
+        + [Workload("table7", B=1, Hq=64, Hk=8, T=1024, d=64, L=64, chunk=0, dtype="bf16",
+                    bwd=True)]
+    )
+}
+# table2_T16384 is also the G = 8 point of the group sweep and the L = 64 point of the
+# depth sweep.
+
 TENSOR_IDS = {"Q": 0, "K": 1, "V": 2, "Kd": 3, "Vd": 4, "dO": 5, "layers_K": 6, "layers_V": 7}
 
 
