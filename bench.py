@@ -55,8 +55,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-l0", action="store_true", help="skip the L=0 comparison run")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="run one plain device-to-device copy of this many MiB first (a "
-                         "kernel of known traffic for scaling hardware byte counters)")
+                    help="run one plain copy of this many MiB first through the packer with "
+                         "L=1 (a kernel of known traffic for scaling hardware byte counters)")
     return ap.parse_args()
 
 
@@ -541,13 +541,16 @@ def main():
         return
     w = inputs.WORKLOADS[args.workload]
     if args.copy_probe_mib > 0:
-        n = args.copy_probe_mib << 20
-        src = torch.empty(n, device="cuda:0", dtype=torch.uint8).fill_(1)
-        dst = torch.empty_like(src)
+        # A kernel of known traffic for scaling hardware byte counters: the packer with
+        # L = 1 is a plain copy (reads and writes copy_probe_mib MiB once).
+        n = (args.copy_probe_mib << 20) // 256
+        src = torch.ones((1, 1, 1, n, 128), device="cuda:0", dtype=torch.bfloat16)
+        dst = torch.empty((1, 1, n, 128), device="cuda:0", dtype=torch.bfloat16)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        binding.moda_pack_depth(binding.problem(1, 1, 1, n, 128, 1, 1.0), src, dst)
         torch.cuda.synchronize()
         del src, dst
+        torch.cuda.empty_cache()
 
     step = Step(w, w.L, seed=0)
     ms, kernels, wall = step.timed(args.steps, args.warmup)

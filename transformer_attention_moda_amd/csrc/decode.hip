@@ -146,42 +146,75 @@ __global__ __launch_bounds__(DEC_NW * 64) void decode_partial_kernel(DecArgs a)
 }
 
 constexpr int COMB_WAVES = 4;
+constexpr int COMB_UNROLL = 8;   // partials whose loads are in flight per wave
 
-// One wave per query row (b, h): merge the group's P partials by the log-sum-exp rule.
+// One workgroup per query row (b, h): merge the group's P partials by the log-sum-exp
+// rule.  All threads find the largest running max; wave w then accumulates partials
+// w, w + 4, ... (loads of COMB_UNROLL partials in flight), and the four waves' sums meet
+// in LDS.
 template <int D>
 __global__ __launch_bounds__(COMB_WAVES * 64) void decode_combine_kernel(DecArgs a)
 {
     constexpr int PE = D / 64;
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * COMB_WAVES + (threadIdx.x >> 6);   // b*Hq + h
-    if (row >= (int64_t)a.B * a.Hq) return;
+    __shared__ float red[COMB_WAVES][D + 1];
+    const int lane = threadIdx.x & 63, w = wave_id();
+    const int64_t row = blockIdx.x;   // b*Hq + h
     const int h = (int)(row % a.Hq), b = (int)(row / a.Hq);
     const int kv = h / a.G, g = h % a.G;
     const int P = a.nsplit * DEC_NW;
     const int64_t first = ((int64_t)b * a.Hk + kv) * P * a.G + g;   // partial p at first + p*G
     float M = -1e30f;
-    for (int p = lane; p < P; p += 64) M = fmaxf(M, a.part_ml[2 * (first + (int64_t)p * a.G)]);
+    for (int p = threadIdx.x; p < P; p += COMB_WAVES * 64)
+        M = fmaxf(M, a.part_ml[2 * (first + (int64_t)p * a.G)]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    if (lane == 0) red[w][D] = M;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < COMB_WAVES; ++i) M = fmaxf(M, red[i][D]);
+    __syncthreads();
     float lsum = 0.f, acc[PE];
 #pragma unroll
     for (int i = 0; i < PE; ++i) acc[i] = 0.f;
-    for (int p = 0; p < P; ++p) {
-        const int64_t pi = first + (int64_t)p * a.G;
-        const float2 ml = *(const float2*)(a.part_ml + 2 * pi);
-        const float wgt = fast_exp2((ml.x - M) * a.c);   // 0 for an empty partial
-        lsum += wgt * ml.y;
-        const float* op = a.part_o + pi * D;
+    for (int p0 = w; p0 < P; p0 += COMB_WAVES * COMB_UNROLL) {
+        float2 ml[COMB_UNROLL];
+        float ov[COMB_UNROLL][PE];
 #pragma unroll
-        for (int i = 0; i < PE; ++i) acc[i] += wgt * op[lane + 64 * i];
-    }
-    const float inv = 1.f / lsum;
+        for (int u = 0; u < COMB_UNROLL; ++u) {
+            const int p = min(p0 + COMB_WAVES * u, P - 1);
+            const int64_t pi = first + (int64_t)p * a.G;
+            ml[u] = *(const float2*)(a.part_ml + 2 * pi);
 #pragma unroll
-    for (int i = 0; i < PE; ++i) {
-        const __bf16 v = (__bf16)(acc[i] * inv);
-        a.O[row * D + lane + 64 * i] = __builtin_bit_cast(uint16_t, v);
+            for (int i = 0; i < PE; ++i) ov[u][i] = a.part_o[pi * D + lane + 64 * i];
+        }
+#pragma unroll
+        for (int u = 0; u < COMB_UNROLL; ++u) {
+            if (p0 + COMB_WAVES * u >= P) continue;
+            const float wgt = fast_exp2((ml[u].x - M) * a.c);   // 0 for an empty partial
+            lsum += wgt * ml[u].y;
+#pragma unroll
+            for (int i = 0; i < PE; ++i) acc[i] += wgt * ov[u][i];
+        }
     }
-    if (lane == 0) a.lse[row] = a.scale * M + __logf(lsum);
+#pragma unroll
+    for (int i = 0; i < PE; ++i) red[w][lane + 64 * i] = acc[i];
+    if (lane == 0) red[w][D] = lsum;
+    __syncthreads();
+    if (w == 0) {
+        float lt = 0.f;
+#pragma unroll
+        for (int j = 0; j < COMB_WAVES; ++j) lt += red[j][D];
+        const float inv = 1.f / lt;
+#pragma unroll
+        for (int i = 0; i < PE; ++i) {
+            float v = 0.f;
+#pragma unroll
+            for (int j = 0; j < COMB_WAVES; ++j) v += red[j][lane + 64 * i];
+            const __bf16 o = (__bf16)(v * inv);
+            a.O[row * D + lane + 64 * i] = __builtin_bit_cast(uint16_t, o);
+        }
+        if (lane == 0) a.lse[row] = a.scale * M + __logf(lt);
+    }
 }
 
 }  // namespace
@@ -241,7 +274,7 @@ hipError_t launch_decode_bf16(const Shape& s, int64_t pos, const void* q, const 
     a.c = s.scale * kLog2e;
     a.scale = s.scale;
     const dim3 grid1((unsigned)(s.B * s.Hk), (unsigned)pl.nsplit);   // nsplit <= 512
-    const unsigned grid2 = (unsigned)((s.B * s.Hq + COMB_WAVES - 1) / COMB_WAVES);
+    const unsigned grid2 = (unsigned)(s.B * s.Hq);   // one workgroup per query row
     timing_begin("decode", st);
     if (s.d == 128)
         hipLaunchKernelGGL((decode_partial_kernel<128>), grid1, dim3(DEC_NW * 64), 0, st, a);

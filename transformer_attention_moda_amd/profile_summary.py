@@ -1,0 +1,186 @@
+"""Per-kernel summaries of rocprofv3 output for libmoda's kernels.
+
+    python -m transformer_attention_moda_amd.profile_summary counters <dir> [<dir> ...]
+    python -m transformer_attention_moda_amd.profile_summary trace <dir>
+    python -m transformer_attention_moda_amd.profile_summary traffic <fetch_dir> <write_dir> \
+        <probe_mib> <workload>
+
+`counters`: every `*counter_collection.csv` under the given rocprofv3 output
+directories (one per --pmc pass); prints, per libmoda kernel, the mean over its
+dispatches of each counter, the dispatch count and the mean duration, then the
+derived rates below.  `trace`: every `*kernel_stats.csv` (rocprofv3
+--kernel-trace --stats), the per-kernel call count and mean duration.
+
+Derived (when the counters are present): GRBM_GUI_ACTIVE / duration = the
+graphics clock the counter ran at (summed over the chip's XCDs, so divided by
+their count); SQ_VALU_MFMA_BUSY_CYCLES / (SQ_BUSY_CU_CYCLES or, failing that,
+GRBM_GUI_ACTIVE x CUs per XCD) = fraction of CU cycles the matrix cores were busy;
+SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS = bank-conflict cycles per LDS instruction
+cycle; SQ_INSTS_* per wave = instruction mix; 4 x SQ_WAVE_CYCLES / SQ_BUSY_CU_CYCLES = mean
+resident waves per CU (SQ_WAVE_CYCLES counts in units of 4 cycles).  `traffic`: HBM bytes
+per launch from a FETCH_SIZE pass and a WRITE_SIZE pass (KiB per dispatch) of
+`bench.py --copy-probe-mib <probe_mib>`, each scaled by what the same counter reads for
+the probe (the packer with L = 1 copying probe_mib MiB: that many bytes read and written),
+in the line format bench.py reads from profiles/traffic.txt.  Nothing here runs on a GPU.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import os
+import re
+import sys
+from collections import defaultdict
+
+XCDS = 8            # MI355X: 8 accelerator complex dies ...
+CUS_PER_XCD = 32    # ... of 32 compute units each
+
+
+def short_name(kernel: str) -> str:
+    """`void moda::(anonymous namespace)::fwd_bf16_kernel<128, 8, false>(...)` ->
+    `fwd_bf16_kernel<128, 8, false>`."""
+    k = kernel.split("(")[0] if "(" in kernel.split("<")[0] else kernel
+    m = re.search(r"([A-Za-z_0-9]+_kernel(<[^()]*>)?)", kernel)
+    return m.group(1) if m else k.strip()[-60:]
+
+
+def _rows(pattern_dirs, suffix):
+    for d in pattern_dirs:
+        for path in glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True):
+            with open(path, newline="") as f:
+                yield from csv.DictReader(f)
+
+
+def counters(dirs):
+    vals = defaultdict(lambda: defaultdict(list))     # kernel -> counter -> per dispatch
+    dur = defaultdict(dict)                           # kernel -> dispatch -> ns
+    for r in _rows(dirs, "counter_collection.csv"):
+        name = r.get("Kernel_Name", "")
+        if "moda" not in name:
+            continue
+        k = short_name(name)
+        key = (r.get("Dispatch_Id") or r.get("Correlation_Id"), r.get("Counter_Name"))
+        vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        s, e = r.get("Start_Timestamp"), r.get("End_Timestamp")
+        if s and e:
+            dur[k][key[0]] = float(e) - float(s)
+    out = []
+    for k in sorted(vals):
+        c = {n: sum(v) / len(v) for n, v in vals[k].items()}
+        ns = sum(dur[k].values()) / max(1, len(dur[k])) if dur[k] else None
+        out.append(f"kernel {k}  dispatches={max(len(v) for v in vals[k].values())}"
+                   + (f"  mean_duration_us={ns / 1e3:.1f}" if ns else ""))
+        for n in sorted(c):
+            out.append(f"  {n:32s} {c[n]:.6g}")
+        g = c.get("GRBM_GUI_ACTIVE")
+        if g and ns:
+            out.append(f"  -> clock (GRBM_GUI_ACTIVE / {XCDS} XCDs / duration): "
+                       f"{g / XCDS / ns:.3f} GHz")
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        cu = c.get("SQ_BUSY_CU_CYCLES") or (g / XCDS * XCDS * CUS_PER_XCD if g else None)
+        if busy and cu:
+            out.append(f"  -> matrix cores busy: {busy / cu:.3f} of CU cycles "
+                       f"(SQ_VALU_MFMA_BUSY_CYCLES / "
+                       f"{'SQ_BUSY_CU_CYCLES' if c.get('SQ_BUSY_CU_CYCLES') else 'GRBM_GUI_ACTIVE x CUs'})")
+        if c.get("SQ_LDS_BANK_CONFLICT") is not None and c.get("SQ_ACTIVE_INST_LDS"):
+            out.append(f"  -> LDS bank-conflict cycles per LDS-active cycle: "
+                       f"{c['SQ_LDS_BANK_CONFLICT'] / c['SQ_ACTIVE_INST_LDS']:.4f}")
+        waves = c.get("SQ_WAVES")
+        if waves:
+            for n in ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
+                      "SQ_INSTS_VMEM"):
+                if n in c:
+                    out.append(f"  -> {n} per wave: {c[n] / waves:.1f}")
+        for n in ("SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS"):
+            if n in c and c.get("SQ_WAVE_CYCLES"):
+                out.append(f"  -> {n} / SQ_WAVE_CYCLES: {c[n] / c['SQ_WAVE_CYCLES']:.3f}")
+        if c.get("SQ_WAVE_CYCLES") and c.get("SQ_BUSY_CU_CYCLES"):
+            out.append(f"  -> resident waves per CU: "
+                       f"{4 * c['SQ_WAVE_CYCLES'] / c['SQ_BUSY_CU_CYCLES']:.2f}")
+    return "\n".join(out)
+
+
+# Sources whose hash marks a traffic line stale once a kernel changes.
+SOURCES = {
+    "pack": ["csrc/pack.hip", "csrc/common.hpp"],
+    "fwd": ["csrc/fwd_bf16.hip", "csrc/common.hpp"],
+}
+for _k in ("bwd_pre", "bwd_depth", "bwd_dq", "bwd_dkdv"):
+    SOURCES[_k] = ["csrc/bwd_bf16.hip", "csrc/common.hpp"]
+LABELS = {"pack_kernel": "pack", "fwd_bf16_kernel": "fwd", "bwd_pre_kernel": "bwd_pre",
+          "bwd_depth_kernel": "bwd_depth", "bwd_dq_kernel": "bwd_dq", "bwd_dkdv_kernel": "bwd_dkdv"}
+
+
+def sources_sha(label):
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for src in SOURCES[label]:
+        h.update(open(os.path.join(here, src), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic(fetch_dir, write_dir, probe_mib, workload):
+    probe_bytes = probe_mib << 20
+    chunks = probe_bytes // 16
+    probe_grid = min((chunks + 255) // 256, 1 << 20) * 256   # the packer's launch
+    per = {}
+    factors = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = defaultdict(list)
+        probe = None
+        for r in _rows([d], "counter_collection.csv"):
+            if r["Counter_Name"] != counter or "moda" not in r["Kernel_Name"]:
+                continue
+            k = LABELS.get(short_name(r["Kernel_Name"]).split("<")[0])
+            if k == "pack" and int(r["Grid_Size"]) == probe_grid and probe is None:
+                probe = float(r["Counter_Value"])
+                continue
+            if k:
+                vals[k].append(float(r["Counter_Value"]))
+        if probe is None:
+            raise SystemExit(f"no copy-probe dispatch (grid {probe_grid}) in {d}")
+        factors[counter] = probe_bytes / (probe * 1024)
+        for k, v in vals.items():
+            per.setdefault(k, {})[counter] = (sum(v) / len(v) * 1024 * factors[counter], len(v))
+    out = [f"# HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE "
+           f"(KiB per dispatch), scaled by a {probe_mib} MiB copy through the packer with L=1 in "
+           f"the same run: factor {factors['FETCH_SIZE']:.4f} (FETCH_SIZE), "
+           f"{factors['WRITE_SIZE']:.4f} (WRITE_SIZE).",
+           "# sha: first 16 hex digits of sha256 over the listed sources; bench.py reports "
+           "traffic only while it matches."]
+    for k in ("pack", "fwd", "bwd_pre", "bwd_depth", "bwd_dq", "bwd_dkdv"):
+        if k not in per:
+            continue
+        f, nf = per[k].get("FETCH_SIZE", (0.0, 0))
+        wr, _ = per[k].get("WRITE_SIZE", (0.0, 0))
+        srcs = ",".join("transformer_attention_moda_amd/" + x for x in SOURCES[k])
+        out.append(f"kernel={k} workload={workload} sha={sources_sha(k)} sources={srcs} "
+                   f"fetch_bytes={f:.4e} write_bytes={wr:.4e} launches_sampled={nf}")
+    return "\n".join(out)
+
+
+def trace(dirs):
+    out = []
+    for r in _rows(dirs, "kernel_stats.csv"):
+        if "moda" not in r.get("Name", ""):
+            continue
+        out.append(f"{short_name(r['Name']):44s} calls={r['Calls']:>5s} "
+                   f"mean_us={float(r['AverageNs']) / 1e3:10.1f} "
+                   f"min_us={float(r['MinNs']) / 1e3:10.1f} max_us={float(r['MaxNs']) / 1e3:10.1f}")
+    return "\n".join(out)
+
+
+def main(argv):
+    if len(argv) < 2 or argv[0] not in ("counters", "trace", "traffic"):
+        print(__doc__)
+        return 2
+    if argv[0] == "traffic":
+        print(traffic(argv[1], argv[2], int(argv[3]), argv[4]))
+    else:
+        print(counters(argv[1:]) if argv[0] == "counters" else trace(argv[1:]))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
