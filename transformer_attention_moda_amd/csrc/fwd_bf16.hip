@@ -82,9 +82,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
     constexpr int BM = NW * 32;
     // K and V tiles of buffers 0 and 1, one array each, so that the compiler can tell a
     // pending direct load into one buffer from reads of the other.  After the sequence
-    // loop they hold the NW private 32-row depth slices, two per array.
+    // loop they hold the waves' private 32-row depth V slices, two per array; the depth K
+    // slices go to ldk with 8 waves, and to the arrays the V slices leave free with 4.
     __shared__ __attribute__((aligned(16))) uint16_t lk0[ELEMS], lv0[ELEMS], lk1[ELEMS], lv1[ELEMS];
-    static_assert(ELEMS == 2 * 32 * TL::PITCH && NW <= 8, "depth slices must fit");
+    __shared__ __attribute__((aligned(16))) uint16_t ldk[NW == 8 ? NW * 32 * D : 8];
+    static_assert(ELEMS == 2 * 32 * TL::PITCH && (NW == 8 || NW == 4), "depth slices must fit");
 
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int col = lane & 31, hf = lane >> 5;
@@ -139,12 +141,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
     // ---- depth rows of this wave's tokens ----
     // The visible depth rows of tokens tw_lo..tw_hi, in blocks of 32: all of
     // [tw_lo*L, (tw_hi+1)*L) without a window; with one, W rows per token gathered as
-    // virtual rows v (token tw_lo + v / W, slot L - W + v % W).  A block's K rows are
-    // MFMA A operands loaded straight into registers, its V rows go to the wave's LDS
-    // slice (direct loads) for the transposed read.  Prefetch: the next block's K loads
-    // are issued as soon as the current scores have consumed the registers, its V loads
-    // as soon as the current PV has read the slice.  Mask: virtual row v is visible to
-    // token t iff (t - tw_lo)*W <= v < (t - tw_lo)*W + W.
+    // virtual rows v (token tw_lo + v / W, slot L - W + v % W).  A block's K and V rows go
+    // to the wave's two LDS slices by direct loads of 1 KiB contiguous rows per
+    // instruction (loading K straight into registers as MFMA operands would request every
+    // 128-byte line four times: 32 bytes of each of 32 rows per instruction).  Prefetch:
+    // the next block's K loads are issued as soon as the current scores have read the K
+    // slice, its V loads as soon as the current PV has read the V slice.  Mask: virtual
+    // row v is visible to token t iff (t - tw_lo)*W <= v < (t - tw_lo)*W + W.
     auto depth_phase = [&]() {
         const int64_t TL_rows = (int64_t)T * L;
         const uint16_t* Kdb = a.Kd + kvbase * (int64_t)L * D;
@@ -169,40 +172,41 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
             }
         };
         uint16_t* const arr = (w >> 1) == 0 ? lk0 : (w >> 1) == 1 ? lv0 : (w >> 1) == 2 ? lk1 : lv1;
-        uint16_t* const slot = arr + (w & 1) * 32 * D;
-        constexpr int NK = D / 16;                     // K loads per block (vector-memory instructions)
-        bf16x8 kr[D / 16];
-        auto issue_v = [&](int i) {   // rows past the wave's last visible row repeat a row (weight 0)
+        uint16_t* const vslot = arr + (w & 1) * 32 * D;
+        uint16_t* const kslot = NW == 8 ? ldk + w * 32 * D : ((w >> 1) == 0 ? lk1 : lv1) + (w & 1) * 32 * D;
+        constexpr int NI1 = 32 / TL::RPI;              // direct-load instructions per 32 rows
+        // Rows past the wave's last visible row repeat a visible row (their weight is 0).
+        auto issue = [&](int i, uint16_t* dst, const uint16_t* src) {
             const int64_t vb = 32 * (int64_t)i;
             if constexpr (!WIN) {
                 const int64_t rb = dlo + vb;
-                stage_rows<D>(slot, 32, Vdb + rb * D,
+                stage_rows<D>(dst, 32, src + rb * D,
                               [&](int r) { return (int)(min(rb + r, TL_rows - 1) - rb) * D; }, lane, 0, 1);
             } else {
                 const int64_t rb = phys(vb);
-                stage_rows<D>(slot, 32, Vdb + rb * D,
+                stage_rows<D>(dst, 32, src + rb * D,
                               [&](int r) { return (int)(phys(min(vb + r, nv - 1)) - rb) * D; }, lane, 0, 1);
             }
         };
-        auto issue_k = [&](int i) {
-            const int64_t v = 32 * (int64_t)i + col;
-            const int64_t r = WIN ? phys(min(v, nv - 1)) : min(dlo + v, TL_rows - 1);
-            const uint16_t* krow = Kdb + r * D + 8 * hf;
-#pragma unroll
-            for (int si = 0; si < D / 16; ++si) kr[si] = __builtin_bit_cast(bf16x8, ld16(krow + 16 * si));
-        };
+        LaneOffsets<D> lof;
+        lof.init(lane);
         if (nblk > 0) {
-            issue_v(0);
-            issue_k(0);
+            issue(0, kslot, Kdb);
+            issue(0, vslot, Vdb);
         }
         for (int i = 0; i < nblk; ++i) {
             const bool more = i + 1 < nblk;
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI1) : "memory");   // K of block i landed
+            wave_lds_sync();
             f32x16 s[2];
 #pragma unroll
             for (int j = 0; j < 16; ++j) s[0][j] = 0.f;
 #pragma unroll
-            for (int si = 0; si < D / 16; ++si) s[0] = mfma32(kr[si], qreg[si], s[0]);
-            if (more) issue_k(i + 1);
+            for (int si = 0; si < D / 16; ++si)
+                s[0] = mfma32(*(const bf16x8*)(kslot + lof.a[si]), qreg[si], s[0]);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");           // the K slice is read
+            wave_lds_sync();
+            if (more) issue(i + 1, kslot, Kdb);
             // first visible virtual row of this lane's token, relative to the lane's rows
             const int64_t lo = (int64_t)(tcol - t_first) * Wn - 32 * (int64_t)i - 4 * hf;
 #pragma unroll
@@ -211,12 +215,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
                 if (rj < lo || rj >= lo + Wn) s[0][j] = -INFINITY;
             }
             softmax_update<D, 1>(s, m, l, o, a.c);
-            if (more) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NK) : "memory");   // V of block i landed
+            if (more) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI1) : "memory");   // V of block i landed
             else wait_vmem();
             wave_lds_sync();
-            pv_block<D>(slot, 0, s[0], o, lane);
+            pv_block<D>(vslot, 0, s[0], o, lane);
             wave_lds_sync();
-            if (more) issue_v(i + 1);
+            if (more) issue(i + 1, vslot, Vdb);
         }
     };
 
