@@ -145,13 +145,13 @@ __global__ __launch_bounds__(DEC_NW * 64) void decode_partial_kernel(DecArgs a)
     }
 }
 
-constexpr int COMB_WAVES = 4;
+constexpr int COMB_WAVES = 16;
 constexpr int COMB_UNROLL = 8;   // partials whose loads are in flight per wave
 
 // One workgroup per query row (b, h): merge the group's P partials by the log-sum-exp
 // rule.  All threads find the largest running max; wave w then accumulates partials
-// w, w + 4, ... (loads of COMB_UNROLL partials in flight), and the four waves' sums meet
-// in LDS.
+// w, w + COMB_WAVES, ... (loads of COMB_UNROLL partials in flight, so that a row's
+// partials take few dependent load rounds), and the waves' sums meet in LDS.
 template <int D>
 __global__ __launch_bounds__(COMB_WAVES * 64) void decode_combine_kernel(DecArgs a)
 {
