@@ -296,6 +296,7 @@ EDGE = [
     (1, 2, 1, 33, 64, 40),      # a token's depth rows span two 32-row blocks
     (1, 4, 4, 20, 128, 64),     # G = 1, each token exactly two depth blocks
     (1, 2, 1, 5, 64, 1024),     # the largest L
+    (1, 1, 1, 300, 64, 1),      # d = 64 with 8-wave workgroups, one depth row per token
 ]
 
 
