@@ -1,7 +1,7 @@
 """Per-kernel summaries of rocprofv3 output for libmoda's kernels.
 
     python -m transformer_attention_moda_amd.profile_summary counters <dir> [<dir> ...]
-    python -m transformer_attention_moda_amd.profile_summary trace <dir>
+    python -m transformer_attention_moda_amd.profile_summary trace <dir> [--by-grid]
     python -m transformer_attention_moda_amd.profile_summary traffic <fetch_dir> <write_dir> \
         <probe_mib> <workload>
 
@@ -9,7 +9,9 @@
 directories (one per --pmc pass); prints, per libmoda kernel, the mean over its
 dispatches of each counter, the dispatch count and the mean duration, then the
 derived rates below.  `trace`: every `*kernel_stats.csv` (rocprofv3
---kernel-trace --stats), the per-kernel call count and mean duration.
+--kernel-trace --stats), the per-kernel call count and mean duration; with --by-grid, from
+`*kernel_trace.csv`, the count and median duration per kernel and launch grid (one line per
+problem size when a run launches a kernel at several).
 
 Derived (when the counters are present): GRBM_GUI_ACTIVE / duration = the
 graphics clock the counter ran at (summed over the chip's XCDs, so divided by
@@ -160,6 +162,22 @@ def traffic(fetch_dir, write_dir, probe_mib, workload):
     return "\n".join(out)
 
 
+def trace_by_grid(dirs):
+    durs = defaultdict(list)
+    for r in _rows(dirs, "kernel_trace.csv"):
+        if "moda" not in r.get("Kernel_Name", ""):
+            continue
+        grid = "x".join(r[f"Grid_Size_{a}"] for a in "XYZ")
+        durs[(short_name(r["Kernel_Name"]), grid)].append(
+            int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = []
+    for (k, grid), v in sorted(durs.items()):
+        v.sort()
+        out.append(f"{k:44s} grid={grid:18s} calls={len(v):5d} median_us={v[len(v) // 2] / 1e3:10.1f} "
+                   f"min_us={v[0] / 1e3:10.1f} max_us={v[-1] / 1e3:10.1f}")
+    return "\n".join(out)
+
+
 def trace(dirs):
     out = []
     for r in _rows(dirs, "kernel_stats.csv"):
@@ -178,7 +196,12 @@ def main(argv):
     if argv[0] == "traffic":
         print(traffic(argv[1], argv[2], int(argv[3]), argv[4]))
     else:
-        print(counters(argv[1:]) if argv[0] == "counters" else trace(argv[1:]))
+        if argv[0] == "counters":
+            print(counters(argv[1:]))
+        elif "--by-grid" in argv:
+            print(trace_by_grid([d for d in argv[1:] if d != "--by-grid"]))
+        else:
+            print(trace(argv[1:]))
     return 0
 
 
