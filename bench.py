@@ -280,13 +280,17 @@ def cpu_model():
     return None
 
 
-def depth_eta(w, scan=0, window=0, rows_per_wg=256):
+def depth_eta(w, scan=0, window=0, rows_per_wg=None):
     """Depth utilisation of the forward's tiling: the fraction of the depth scores it
     computes that the mask keeps (the "Depth Utilization" of the pages' efficiency tables).
     Each 32-row query block (one wave) scores 32x32 MFMA blocks of depth rows: of its own
     tokens (scan 0), of its workgroup chunk's (1), or all of the KV head's (2); every
-    query sees exactly W of them."""
+    query sees exactly W of them.  rows_per_wg: the library's tiling for w by default."""
     G, T, L = w.G, w.T, w.L
+    if rows_per_wg is None:
+        from transformer_attention_moda_amd import binding as mb
+        rows_per_wg = G * mb.moda_fwd_chunk_tokens(
+            mb.problem(w.B, w.Hq, w.Hk, w.T, w.d, w.L, w.scale, chunk=w.chunk))
     W = window if window else L
     if L == 0:
         return None

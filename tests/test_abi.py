@@ -145,7 +145,8 @@ def test_pack_checks():
 
 
 def test_chunk_tokens_and_status_strings():
-    assert mb.moda_fwd_chunk_tokens(prob(Hq=4, Hk=2)) == 128
+    assert mb.moda_fwd_chunk_tokens(prob(Hq=4, Hk=2, d=128)) == 128   # 256 rows at d = 128
+    assert mb.moda_fwd_chunk_tokens(prob(Hq=4, Hk=2)) == 64           # 128 rows at d = 64
     assert mb.moda_fwd_chunk_tokens(prob(Hq=4, Hk=2, chunk=64)) == 64
     assert mb.moda_fwd_chunk_tokens(prob(Hq=16, Hk=4, chunk=64)) == 64
     assert mb.moda_fwd_chunk_tokens(prob(Hq=16, Hk=4, chunk=16)) == 32

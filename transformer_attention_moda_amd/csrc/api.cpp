@@ -127,7 +127,9 @@ moda_status_t hip_status(hipError_t e, const char* what)
 
 int rows_per_workgroup(const moda_problem_t* p, int G)
 {
-    if (p->chunk == 0) return 256;
+    // Default: 256 folded rows (8 waves, two per SIMD) at d = 128; 128 rows at d = 64, whose
+    // 4-wave workgroups fit three per CU (168 registers a wave, three waves per SIMD).
+    if (p->chunk == 0) return p->d == 64 ? 128 : 256;
     return (int64_t)p->chunk * G >= 256 ? 256 : 128;
 }
 

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a)
 
 // ---------------------------------------------------------------- bwd_dq
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
+__global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void bwd_dq_kernel(BwdArgs a)
 {
     using TL = LdsTile<D>;
     constexpr int ELEMS = BN * TL::PITCH;
@@ -277,11 +277,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a)
 // ---------------------------------------------------------------- bwd_dkdv
 constexpr int BQ = 64;  // folded query rows per staged tile (bwd_dkdv)
 
-// At d = 128 the accumulators and operands need about 480 registers: one wave per SIMD.
-// At d = 64 two waves per SIMD fit in 256 registers each (a few spills outside the tile
-// loop's main path), and the second wave hides LDS latency: 10-15% faster at T >= 16K.
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a)
+// WPS: waves per SIMD the registers are budgeted for.  At d = 128 the accumulators and
+// operands need about 480 registers: one.  At d = 64 two fit in 256 registers each (a few
+// spills outside the tile loop's main path) and the second wave hides LDS latency, 10-15%
+// faster once there are enough workgroups; on small grids, where every workgroup is
+// resident at once and the heaviest key block sets the time, one wave with the whole
+// register file is faster.
+template <int D, int NW, int WPS>
+__global__ __launch_bounds__(NW * 64, WPS) void bwd_dkdv_kernel(BwdArgs a)
 {
     using TL = LdsTile<D>;
     static_assert(BQ % (TL::RPI * NW) == 0, "tile staging must divide evenly");
@@ -701,7 +704,8 @@ hipError_t run(const Shape& s, BwdArgs a, hipStream_t st)
         timing_end(st);
     }
     {
-        constexpr int NW = 8;
+        // d = 64: 4-wave workgroups, three per CU (168 registers a wave); d = 128: 8 waves.
+        constexpr int NW = D == 64 ? 4 : 8;
         a.nblocks = (int)((TG + NW * 32 - 1) / (NW * 32));
         timing_begin("bwd_dq", st);
         hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3((unsigned)(nunits * a.nblocks)),
@@ -711,9 +715,14 @@ hipError_t run(const Shape& s, BwdArgs a, hipStream_t st)
     {
         constexpr int NW = 4;
         a.nblocks = (int)((s.T + NW * 32 - 1) / (NW * 32));
+        const unsigned grid = (unsigned)(nunits * a.nblocks);
         timing_begin("bwd_dkdv", st);
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW>), dim3((unsigned)(nunits * a.nblocks)),
-                           dim3(NW * 64), 0, st, a);
+        bool two = false;
+        if constexpr (D == 64) two = grid >= 1024;   // four workgroups per CU or more
+        if (two)
+            hipLaunchKernelGGL((bwd_dkdv_kernel<64, NW, 2>), dim3(grid), dim3(NW * 64), 0, st, a);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, 1>), dim3(grid), dim3(NW * 64), 0, st, a);
         timing_end(st);
     }
     return hipGetLastError();

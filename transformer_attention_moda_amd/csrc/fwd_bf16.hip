@@ -74,7 +74,7 @@ __device__ __forceinline__ float row_sum_bf16(const bf16x8& p, float acc)
 // Eight waves per CU either way: one 8-wave workgroup (256 rows) or two 4-wave
 // workgroups (128 rows), two waves per SIMD and at most 256 registers per wave.
 template <int D, int NW, bool WIN>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
+__global__ __launch_bounds__(NW * 64, (D == 64 && NW == 4) ? 3 : 8 / NW) void fwd_bf16_kernel(FwdArgs a)
 {
     using TL = LdsTile<D>;
     constexpr int ELEMS = BN * TL::PITCH;      // one K or V tile
