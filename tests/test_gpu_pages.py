@@ -60,3 +60,41 @@ def test_depth_scan_ablation_gives_the_operator(scan):
     Or, lr = oracle.fwd(h["Q"], h["K"], h["V"], h["Kd"], h["Vd"], w.L, w.scale)
     check(f"table7 scan {scan} O", to64(O), Or, w.dtype)
     check(f"table7 scan {scan} lse", to64(lse), lr, w.dtype, fp32_output=True)
+
+
+def test_every_key_gradient_under_sparse_upstream_d64_two_wave_backward():
+    """The G=2 workload (T=16384, d=64, 1024 key-stationary workgroups, so the backward's
+    key pass runs its two-waves-per-SIMD form): dO zero outside a token set S, so the
+    oracle's backward restricted to S is exact for every gradient, and every dK and dV row
+    of every KV group -- the heavy first key blocks included -- is compared, with dQ and the
+    depth gradients of S (the other tokens' depth rows and dQ rows must be exactly zero)."""
+    w = PW["table2_G2"]
+    G, T, L = w.G, w.T, w.L
+    assert (T + 127) // 128 * w.B * w.Hk >= 1024
+    x = inputs.make(w, seed=62, device=DEV, names=("Q", "K", "V", "Kd", "Vd", "dO"))
+    O, lse = run_fwd(x, w)
+    tok = set(range(4)) | set(range(T - 4, T)) | set(np.linspace(0, T - 1, 40).astype(int))
+    for c in (1, 37, 64, 127):
+        tok |= {c * 128 - 1, c * 128}
+    S = np.array(sorted(t for t in tok if 0 <= t < T))
+    idx = torch.from_numpy(S).to(DEV)
+    dO = torch.zeros_like(x["dO"])
+    dO[:, :, idx] = x["dO"][:, :, idx]
+    dQ, dK, dV, dKd, dVd = run_bwd(dict(x, dO=dO), w, O, lse)
+    torch.cuda.synchronize()
+    h = oracle_inputs(dict(x, dO=dO))
+    rows = (torch.from_numpy(S)[:, None] * L + torch.arange(L)[None, :]).reshape(-1).to(DEV)
+    other = torch.ones(T * L, dtype=torch.bool, device=DEV)
+    other[rows] = False
+    for kv in range(w.Hk):
+        g = oracle.bwd_tokens(h["Q"], h["K"], h["V"], h["Kd"], h["Vd"], h["dO"], L, w.scale, 0,
+                              kv, S)
+        hs = slice(kv * G, (kv + 1) * G)
+        tag = f"table2_G2 sparse dO ({len(S)} tokens) kv={kv}"
+        check(f"{tag} dK (all {T} keys)", to64(dK[0, kv]), g["dK"], w.dtype)
+        check(f"{tag} dV (all {T} keys)", to64(dV[0, kv]), g["dV"], w.dtype)
+        check(f"{tag} dQ", to64(dQ[0, hs][:, idx]), g["dQ"], w.dtype)
+        check(f"{tag} dKd", to64(dKd[0, kv, rows]), g["dKd"], w.dtype)
+        check(f"{tag} dVd", to64(dVd[0, kv, rows]), g["dVd"], w.dtype)
+        assert not torch.any(dKd[0, kv, other] != 0) and not torch.any(dVd[0, kv, other] != 0)
+        assert not torch.any(dQ[0, hs][:, ~torch.isin(torch.arange(T, device=DEV), idx)] != 0)
