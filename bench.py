@@ -582,6 +582,8 @@ def main():
 
     def roof(label, k, wl):
         bound, amount, _ = kernel_work(label, wl)
+        if bound is None:   # a kernel without a roofline of its own (the split pass's reduce)
+            return {"bound": None}
         if bound == "mfma":
             ach, peak, unit = amount / (k["avg_ms"] * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
         else:

@@ -111,7 +111,10 @@ moda_status_t moda_fwd(const moda_problem_t* p, const void* Q, const void* K, co
 
 /* Bytes of device workspace moda_bwd needs for problem p (0 for an invalid p):
  * 8 bytes per query row, and for MODA_BF16 with L > 0 another 4*d bytes per
- * query row (fp32 partial gradients handed between the backward's kernels). */
+ * query row (fp32 partial gradients handed between the backward's kernels); for
+ * MODA_BF16 problems too small to fill the GPU with their key blocks (fewer than
+ * 1024 blocks of 128 keys over B*Hk), also 8*d bytes per key row of each piece
+ * the heavy key blocks' query walks are split into (fp32 partial dK, dV). */
 size_t moda_bwd_workspace_bytes(const moda_problem_t* p);
 
 /*

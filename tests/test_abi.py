@@ -103,6 +103,13 @@ def test_workspace_bytes():
     n0 = mb.moda_bwd_workspace_bytes(prob(B=2, Hq=8, Hk=4, T=100, L=0))
     nf = mb.moda_bwd_workspace_bytes(prob(B=2, Hq=8, Hk=4, T=100, dtype=mb.MODA_F32))
     assert 2 * rows * 4 <= n0 < 2 * rows * 4 + 256 and n0 == nf
+    # A small bf16 problem (32 key blocks of 128 keys, G = 8): its key pass is split into
+    # pieces whose fp32 partial dK, dV (2 x 128 keys x d floats a piece) follow the rows.
+    nsplit = mb.moda_bwd_workspace_bytes(prob(Hq=8, Hk=1, T=4096, L=0))
+    rows1 = 8 * 4096
+    base = (2 * rows1 * 4 + 255) // 256 * 256
+    assert nsplit > base and (nsplit - base) % (2 * 128 * 64 * 4) == 0
+    assert nsplit - base >= 2 * 32 * 2 * 128 * 64 * 4   # at least two pieces a key block, on average
     assert mb.moda_bwd_workspace_bytes(prob(B=0)) == 0
     assert mb.load().moda_bwd_workspace_bytes(None) == 0
 

@@ -62,19 +62,20 @@ def test_depth_scan_ablation_gives_the_operator(scan):
     check(f"table7 scan {scan} lse", to64(lse), lr, w.dtype, fp32_output=True)
 
 
-def test_every_key_gradient_under_sparse_upstream_d64_two_wave_backward():
-    """The G=2 workload (T=16384, d=64, 1024 key-stationary workgroups, so the backward's
-    key pass runs its two-waves-per-SIMD form): dO zero outside a token set S, so the
-    oracle's backward restricted to S is exact for every gradient, and every dK and dV row
-    of every KV group -- the heavy first key blocks included -- is compared, with dQ and the
-    depth gradients of S (the other tokens' depth rows and dQ rows must be exactly zero)."""
-    w = PW["table2_G2"]
+@pytest.mark.parametrize("name", ["table2_G2", "table2_T4096", "table7"])
+def test_every_key_gradient_under_sparse_upstream(name):
+    """dO zero outside a token set S, so the oracle's backward restricted to S is exact for
+    every gradient: every dK and dV row of every KV group -- the heavy first key blocks
+    included -- is compared, with dQ and the depth gradients of S (the other tokens' depth
+    rows and dQ rows must be exactly zero).  G=2 (T=16384, 1024 key-stationary workgroups)
+    runs the key pass at two waves per SIMD; T=4096 and the Table 7 shape (256 and 64 key
+    blocks) run it split, the heavy blocks' query walks in pieces summed by the reduce."""
+    w = PW[name]
     G, T, L = w.G, w.T, w.L
-    assert (T + 127) // 128 * w.B * w.Hk >= 1024
     x = inputs.make(w, seed=62, device=DEV, names=("Q", "K", "V", "Kd", "Vd", "dO"))
     O, lse = run_fwd(x, w)
     tok = set(range(4)) | set(range(T - 4, T)) | set(np.linspace(0, T - 1, 40).astype(int))
-    for c in (1, 37, 64, 127):
+    for c in (1, 3, 5, 37, 64, 127):
         tok |= {c * 128 - 1, c * 128}
     S = np.array(sorted(t for t in tok if 0 <= t < T))
     idx = torch.from_numpy(S).to(DEV)
@@ -90,7 +91,7 @@ def test_every_key_gradient_under_sparse_upstream_d64_two_wave_backward():
         g = oracle.bwd_tokens(h["Q"], h["K"], h["V"], h["Kd"], h["Vd"], h["dO"], L, w.scale, 0,
                               kv, S)
         hs = slice(kv * G, (kv + 1) * G)
-        tag = f"table2_G2 sparse dO ({len(S)} tokens) kv={kv}"
+        tag = f"{name} sparse dO ({len(S)} tokens) kv={kv}"
         check(f"{tag} dK (all {T} keys)", to64(dK[0, kv]), g["dK"], w.dtype)
         check(f"{tag} dV (all {T} keys)", to64(dV[0, kv]), g["dV"], w.dtype)
         check(f"{tag} dQ", to64(dQ[0, hs][:, idx]), g["dQ"], w.dtype)

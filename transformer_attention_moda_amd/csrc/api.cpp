@@ -135,12 +135,16 @@ int rows_per_workgroup(const moda_problem_t* p, int G)
 
 // Two fp32 values per query row: the log-sum-exp in log2 units and D = <dO, O>;
 // in bfloat16 with depth rows, then (256-byte aligned) an fp32 row of d values per
-// query row: the depth rows' part of dQ, passed from bwd_depth to bwd_dq.
+// query row: the depth rows' part of dQ, passed from bwd_depth to bwd_dq; then, for
+// bfloat16 problems whose key pass is split (small grids), the pieces' partial dK, dV.
 size_t bwd_ws_bytes(const moda::Shape& s, int32_t dtype)
 {
     const size_t rows = (size_t)(s.B * s.Hq * s.T);
     size_t n = (2 * rows * sizeof(float) + 255) & ~size_t(255);
     if (dtype == MODA_BF16 && s.L > 0) n += rows * (size_t)s.d * sizeof(float);
+    n = (n + 255) & ~size_t(255);
+    // bfloat16 on small grids: the split key-stationary pass's fp32 partial dK, dV.
+    if (dtype == MODA_BF16) n += (size_t)moda::plan_dkdv(s).part_floats * sizeof(float);
     return (n + 255) & ~size_t(255);
 }
 

@@ -28,6 +28,7 @@
 // ends.  A depth window (the last W of L slots): bwd_depth gives the hidden
 // slots weight 0, so their dKd, dVd rows are written as exact zeros and they add
 // nothing to dQ.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -60,6 +61,9 @@ struct BwdArgs {
     float c;       // scale * log2(e)
     float scale;
     int64_t rows;  // B*Hq*T
+    float* part;       // bwd_dkdv split: fp32 partial dK, dV per piece [grid][2][128][d]
+    int piece_tiles;   // bwd_dkdv: query tiles per piece of a split key block (0: no split)
+    int nkeyblocks;    // bwd_dkdv: key blocks per (b, kv)
 };
 
 constexpr int BN = 64;  // sequence keys per tile (bwd_dq)
@@ -283,7 +287,9 @@ constexpr int BQ = 64;  // folded query rows per staged tile (bwd_dkdv)
 // faster once there are enough workgroups; on small grids, where every workgroup is
 // resident at once and the heaviest key block sets the time, one wave with the whole
 // register file is faster.
-template <int D, int NW, int WPS>
+// SPLIT: the launch splits key blocks' query walks into pieces (small grids); a separate
+// instance, so that the unsplit kernels carry none of its code.
+template <int D, int NW, int WPS, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, WPS) void bwd_dkdv_kernel(BwdArgs a)
 {
     using TL = LdsTile<D>;
@@ -302,7 +308,28 @@ __global__ __launch_bounds__(NW * 64, WPS) void bwd_dkdv_kernel(BwdArgs a)
 
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int unit = logical / a.nblocks;
-    const int kblk = logical % a.nblocks;        // small key blocks see the most queries: first
+    int kblk = logical % a.nblocks;   // small key blocks see the most queries: first
+    // Split walks (small grids): work block r of a unit is piece r - (pieces of the key
+    // blocks before it) of the first key block whose pieces reach past r.
+    int piece = 0, npieces = 1;
+    if constexpr (SPLIT) {
+        const int64_t TGs = (int64_t)T * G;
+        const bool ncs = a.noncausal != 0;
+        // Query tiles key block k walks: from the first folded row that sees one of its keys.
+        auto tiles_of = [&](int k) {
+            return (int)((TGs - (ncs ? 0 : (int64_t)k * BK * G) + BQ - 1) / BQ);
+        };
+        int r = kblk;
+        for (kblk = 0;; ++kblk) {
+            const int n = (tiles_of(kblk) + a.piece_tiles - 1) / a.piece_tiles;
+            if (r < n) {
+                npieces = n;
+                piece = r;
+                break;
+            }
+            r -= n;
+        }
+    }
     const int b = unit / a.Hk, kv = unit % a.Hk;
     const int k0 = kblk * BK, kw = k0 + 32 * w, key = kw + col;
     const bool kvalid = key < T;
@@ -331,6 +358,9 @@ __global__ __launch_bounds__(NW * 64, WPS) void bwd_dkdv_kernel(BwdArgs a)
     const int64_t f_start = nc ? 0 : (int64_t)k0 * G;
     const int ntiles = (int)((TG - f_start + BQ - 1) / BQ);
     const int n_mask = nc ? 0 : min(ntiles, ((BK - 1) * G + BQ - 1) / BQ);
+    // This work block's tiles [it_begin, it_end) of the walk.
+    const int it_begin = SPLIT ? piece * a.piece_tiles : 0;
+    const int it_end = SPLIT && npieces > 1 ? min(ntiles, it_begin + a.piece_tiles) : ntiles;
     const int64_t qhead0 = (int64_t)b * a.Hq + (int64_t)kv * G;
 
     // Folded row f0 + r (f0 a multiple of BQ, G | BQ) is query head qhead0 + r%G at token
@@ -385,7 +415,7 @@ __global__ __launch_bounds__(NW * 64, WPS) void bwd_dkdv_kernel(BwdArgs a)
         const uint16_t* qs = BUF ? lb1 : lb0;
         const uint16_t* ds = qs + TILE;
         const float* sr = BUF ? sr1 : sr0;
-        if (it + 1 < ntiles) {
+        if (it + 1 < it_end) {
             if (BUF) stage(it + 1, lb0, sr0);
             else stage(it + 1, lb1, sr1);
         }
@@ -488,28 +518,76 @@ __global__ __launch_bounds__(NW * 64, WPS) void bwd_dkdv_kernel(BwdArgs a)
     using I1 = std::integral_constant<int, 1>;
     using BF = std::integral_constant<bool, false>;
     using BT = std::integral_constant<bool, true>;
-    if (ntiles > 0) {
-        stage(0, lb0, sr0);
+    // Tile it is staged into buffer it & 1.
+    if (it_begin < it_end) {
+        if (it_begin & 1) stage(it_begin, lb1, sr1);
+        else stage(it_begin, lb0, sr0);
     }
     wait_vmem();
     __syncthreads();
-    int it = 0;
-    for (; it < n_mask; ++it) {
+    int it = it_begin;
+    for (; it < (SPLIT ? min(n_mask, it_end) : n_mask); ++it) {
         if (it & 1) step(I1(), BT(), it);
         else step(I0(), BT(), it);
     }
-    if (it < ntiles && (it & 1)) {
+    if (it < it_end && (it & 1)) {
         step(I1(), BF(), it);
         ++it;
     }
-    for (; it + 1 < ntiles; it += 2) {
+    for (; it + 1 < it_end; it += 2) {
         step(I0(), BF(), it);
         step(I1(), BF(), it + 1);
     }
-    if (it < ntiles) step(I0(), BF(), it);
+    if (it < it_end) step(I0(), BF(), it);
     if (kvalid) {
-        store_row_bf16<D>(a.dK + (kvbase + key) * D, dk, a.scale, lane);
-        store_row_bf16<D>(a.dV + (kvbase + key) * D, dv, 1.f, lane);
+        if (!SPLIT || npieces == 1) {
+            store_row_bf16<D>(a.dK + (kvbase + key) * D, dk, a.scale, lane);
+            store_row_bf16<D>(a.dV + (kvbase + key) * D, dv, 1.f, lane);
+        } else {   // partial sums of this piece, unscaled; dkdv_reduce_kernel adds the pieces
+            float* pk = a.part + ((int64_t)logical * 2 * BK + (key - k0)) * D;
+            store_row_f32<D>(pk, dk, lane);
+            store_row_f32<D>(pk + (int64_t)BK * D, dv, lane);
+        }
+    }
+}
+
+// Split key blocks (bwd_dkdv with piece_tiles > 0): dK, dV of each key block walked in
+// more than one piece are the sum of its pieces' partials, added in piece order (so the
+// result does not depend on scheduling).  One workgroup per (b, kv, key block).
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(BwdArgs a)
+{
+    constexpr int BK = 128;
+    const int unit = blockIdx.x / a.nkeyblocks, kblk = blockIdx.x % a.nkeyblocks;
+    const int64_t TG = (int64_t)a.T * a.G;
+    const bool nc = a.noncausal != 0;
+    int first = 0, np = 0;
+    for (int k = 0; k <= kblk; ++k) {
+        const int nt = (int)((TG - (nc ? 0 : (int64_t)k * BK * a.G) + BQ - 1) / BQ);
+        const int n = (nt + a.piece_tiles - 1) / a.piece_tiles;
+        if (k == kblk) np = n;
+        else first += n;
+    }
+    if (np <= 1) return;   // written directly by its one piece
+    const int b = unit / a.Hk, kv = unit % a.Hk;
+    const int k0 = kblk * BK;
+    const int64_t kvbase = ((int64_t)b * a.Hk + kv) * a.T;
+    const float* p0 = a.part + ((int64_t)unit * a.nblocks + first) * 2 * BK * D;
+    for (int e = 4 * threadIdx.x; e < BK * D; e += 4 * 256) {
+        const int key = k0 + e / D;
+        if (key >= a.T) break;
+        float4 sk = make_float4(0.f, 0.f, 0.f, 0.f), sv = sk;
+        for (int p = 0; p < np; ++p) {
+            const float4 vk = *(const float4*)(p0 + (int64_t)p * 2 * BK * D + e);
+            const float4 vv = *(const float4*)(p0 + (int64_t)p * 2 * BK * D + BK * D + e);
+            sk.x += vk.x; sk.y += vk.y; sk.z += vk.z; sk.w += vk.w;
+            sv.x += vv.x; sv.y += vv.y; sv.z += vv.z; sv.w += vv.w;
+        }
+        const bf16x4 ok = {(__bf16)(sk.x * a.scale), (__bf16)(sk.y * a.scale), (__bf16)(sk.z * a.scale),
+                           (__bf16)(sk.w * a.scale)};
+        const bf16x4 ov = {(__bf16)sv.x, (__bf16)sv.y, (__bf16)sv.z, (__bf16)sv.w};
+        *(bf16x4*)(a.dK + (kvbase + key) * D + e % D) = ok;
+        *(bf16x4*)(a.dV + (kvbase + key) * D + e % D) = ov;
     }
 }
 
@@ -714,21 +792,59 @@ hipError_t run(const Shape& s, BwdArgs a, hipStream_t st)
     }
     {
         constexpr int NW = 4;
-        a.nblocks = (int)((s.T + NW * 32 - 1) / (NW * 32));
+        const DkdvPlan pl = plan_dkdv(s);
+        a.nkeyblocks = pl.key_blocks;
+        a.piece_tiles = pl.piece_tiles;
+        a.nblocks = pl.pieces_per_unit;
         const unsigned grid = (unsigned)(nunits * a.nblocks);
         timing_begin("bwd_dkdv", st);
         bool two = false;
         if constexpr (D == 64) two = grid >= 1024;   // four workgroups per CU or more
         if (two)
-            hipLaunchKernelGGL((bwd_dkdv_kernel<64, NW, 2>), dim3(grid), dim3(NW * 64), 0, st, a);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<64, NW, 2, false>), dim3(grid), dim3(NW * 64), 0, st, a);
+        else if (pl.piece_tiles > 0)
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, 1, true>), dim3(grid), dim3(NW * 64), 0, st, a);
         else
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, 1>), dim3(grid), dim3(NW * 64), 0, st, a);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, 1, false>), dim3(grid), dim3(NW * 64), 0, st, a);
         timing_end(st);
+        if (pl.piece_tiles > 0) {
+            timing_begin("dkdv_reduce", st);
+            hipLaunchKernelGGL((dkdv_reduce_kernel<D>), dim3((unsigned)(nunits * pl.key_blocks)),
+                               dim3(256), 0, st, a);
+            timing_end(st);
+        }
     }
     return hipGetLastError();
 }
 
 }  // namespace
+
+// Small grids (under 1024 key-stationary workgroups, fewer than four per CU): every
+// workgroup is resident at once and the heaviest key block -- the first, whose walk
+// covers every query tile -- sets the pass's time.  Split each walk into pieces of P
+// tiles, P about half a CU's share of all tiles (at least 8), when the heaviest walk is
+// at least two pieces; the pieces' fp32 partials are summed by dkdv_reduce_kernel.
+DkdvPlan plan_dkdv(const Shape& s)
+{
+    constexpr int64_t BK = 128;   // keys per workgroup of bwd_dkdv (4 waves x 32)
+    DkdvPlan p;
+    const int64_t TG = s.T * s.G, units = s.B * s.Hk;
+    p.key_blocks = (int)((s.T + BK - 1) / BK);
+    p.pieces_per_unit = p.key_blocks;
+    if (units * p.key_blocks >= 1024) return p;
+    auto tiles = [&](int64_t k) { return (TG - (s.noncausal ? 0 : k * BK * s.G) + BQ - 1) / BQ; };
+    int64_t total = 0;
+    for (int64_t k = 0; k < p.key_blocks; ++k) total += tiles(k);
+    total *= units;
+    const int64_t P = std::max<int64_t>(8, (total + 511) / 512);
+    if (tiles(0) < 2 * P) return p;
+    int64_t ppu = 0;
+    for (int64_t k = 0; k < p.key_blocks; ++k) ppu += (tiles(k) + P - 1) / P;
+    p.piece_tiles = (int)P;
+    p.pieces_per_unit = (int)ppu;
+    p.part_floats = units * ppu * 2 * BK * s.d;
+    return p;
+}
 
 hipError_t launch_bwd_bf16(const Shape& s, const void* Q, const void* K, const void* V,
                            const void* Kd, const void* Vd, const void* O, const float* lse,
@@ -753,6 +869,7 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* Q, const void* K, const v
     a.lse2 = ws;
     a.Dv = ws + a.rows;
     a.dqd = ws + ((2 * a.rows + 63) & ~int64_t(63));   // 256-byte aligned
+    a.part = a.dqd + (((s.L > 0 ? a.rows * s.d : 0) + 63) & ~int64_t(63));
     a.Hq = (int)s.Hq;
     a.Hk = (int)s.Hk;
     a.T = (int)s.T;
@@ -765,6 +882,8 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* Q, const void* K, const v
     a.c = s.scale * kLog2e;
     a.scale = s.scale;
     a.nblocks = 1;
+    a.piece_tiles = 0;
+    a.nkeyblocks = 0;
     return s.d == 128 ? run<128>(s, a, st) : run<64>(s, a, st);
 }
 

@@ -252,6 +252,20 @@ __device__ __forceinline__ void store_row_bf16(uint16_t* row, const f32x16 (&acc
         }
 }
 
+// The same row in fp32 (no rounding, no factor): 16-byte stores.
+template <int D>
+__device__ __forceinline__ void store_row_f32(float* row, const f32x16 (&acc)[D / 32], int lane)
+{
+    const int hf = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            *(float4*)(row + 32 * db + 8 * jj + 4 * hf) =
+                make_float4(acc[db][4 * jj + 0], acc[db][4 * jj + 1], acc[db][4 * jj + 2],
+                            acc[db][4 * jj + 3]);
+}
+
 template <int N>
 __device__ __forceinline__ void zero(f32x16 (&a)[N])
 {

@@ -26,7 +26,19 @@ hipError_t launch_fwd_bf16(const Shape& s, const void* Q, const void* K, const v
                            const void* Kd, const void* Vd, void* O, float* lse, int rows_per_wg,
                            hipStream_t st, int scan = 0);
 
-// Backward, bfloat16 storage.  ws: B*Hq*T floats.
+// The key-stationary backward pass on small grids: a key block's walk over the query
+// tiles split into pieces of piece_tiles tiles (0: not split), pieces_per_unit work blocks
+// per (b, kv); part_floats fp32 of partial dK, dV in the workspace.
+struct DkdvPlan {
+    int piece_tiles = 0;
+    int key_blocks = 0;
+    int pieces_per_unit = 0;
+    int64_t part_floats = 0;
+};
+DkdvPlan plan_dkdv(const Shape& s);
+
+// Backward, bfloat16 storage.  ws: the workspace (lse2 and D per row, the depth part of
+// dQ when L > 0, then the split pass's partials; sizes as the ABI's workspace query).
 hipError_t launch_bwd_bf16(const Shape& s, const void* Q, const void* K, const void* V,
                            const void* Kd, const void* Vd, const void* O, const float* lse,
                            const void* dO, void* dQ, void* dK, void* dV, void* dKd, void* dVd,
