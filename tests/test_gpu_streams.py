@@ -11,8 +11,13 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _setup(L=4):
-    w = inputs.Workload("streams", 1, 4, 2, 300, 128, L, chunk=0, dtype="bf16")
+# (B, Hq, Hk, T, d): one shape whose backward runs the key pass whole, and one small enough
+# (8 key blocks of one KV head) that it splits the walks and adds the pieces in a second kernel.
+SHAPES = [(1, 4, 2, 300, 128), (1, 8, 1, 1024, 64)]
+
+
+def _setup(L=4, shape=SHAPES[0]):
+    w = inputs.Workload("streams", *shape, L, chunk=0, dtype="bf16")
     x = inputs.make(w, seed=23, device=DEV, names=("Q", "K", "V", "Kd", "Vd", "dO"))
     p = binding.problem_for(x["Q"], x["K"], w.L, w.scale)
     out = {
@@ -35,8 +40,9 @@ def _run(p, x, o):
 NAMES = ("O", "lse", "dQ", "dK", "dV", "dKd", "dVd")
 
 
-def test_calls_run_on_the_callers_side_stream():
-    p, x, o = _setup()
+@pytest.mark.parametrize("shape", SHAPES)
+def test_calls_run_on_the_callers_side_stream(shape):
+    p, x, o = _setup(shape=shape)
     _run(p, x, o)
     torch.cuda.synchronize()
     ref = {k: o[k].clone() for k in NAMES}
@@ -51,8 +57,9 @@ def test_calls_run_on_the_callers_side_stream():
         assert torch.equal(o[k], ref[k]), k
 
 
-def test_graph_capture_replays_match_eager():
-    p, x, o = _setup()
+@pytest.mark.parametrize("shape", SHAPES)
+def test_graph_capture_replays_match_eager(shape):
+    p, x, o = _setup(shape=shape)
     _run(p, x, o)
     torch.cuda.synchronize()
     ref = {k: o[k].clone() for k in NAMES}
@@ -70,4 +77,42 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         for k in NAMES:
             assert torch.equal(o[k], ref[k]), (rep, k)
+        assert torch.isfinite(b)
+
+
+def test_append_and_decode_step_in_a_captured_graph():
+    """A serving step as a graph: append one layer's entries for the last 4 tokens into a
+    slot of the packed depth cache, then decode the last token; three replays with eager
+    work between them match the eager step bitwise."""
+    w = inputs.Workload("decode_graph", 1, 8, 2, 300, 128, 4, chunk=0, dtype="bf16")
+    x = inputs.make(w, seed=29, device=DEV, names=("Q", "K", "V", "Kd", "Vd"))
+    p = binding.problem_for(x["Q"], x["K"], w.L, w.scale)
+    layer = inputs.normal((1, w.Hk, 4, w.d), seed=29, tensor="layers_K", device=DEV)
+    q = x["Q"][:, :, -1].contiguous()
+    packed = x["Kd"].clone()
+    O = torch.empty_like(q)
+    lse = torch.empty((1, w.Hq), device=DEV, dtype=torch.float32)
+    ws = torch.empty(binding.moda_decode_workspace_bytes(p), device=DEV, dtype=torch.uint8)
+
+    def step():
+        binding.moda_depth_append(p, layer, 2, w.T - 4, packed)
+        binding.moda_decode(p, w.T - 1, q, x["K"], x["V"], packed, x["Vd"], O, lse, ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (packed.clone(), O.clone(), lse.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    a = torch.randn(256, 256, device=DEV)
+    for rep in range(3):
+        packed.copy_(x["Kd"])
+        O.zero_()
+        lse.zero_()
+        b = (a @ a).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(packed, ref[0]) and torch.equal(O, ref[1]) and torch.equal(lse, ref[2]), rep
         assert torch.isfinite(b)
