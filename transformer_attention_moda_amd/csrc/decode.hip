@@ -145,20 +145,26 @@ __global__ __launch_bounds__(DEC_NW * 64) void decode_partial_kernel(DecArgs a)
     }
 }
 
-constexpr int COMB_WAVES = 16;
-constexpr int COMB_UNROLL = 8;   // partials whose loads are in flight per wave
+constexpr int COMB_WAVES = 8;
+constexpr int COMB_UNROLL = 8;   // partials whose loads are in flight per half-wave
 
-// One workgroup per query row (b, h): merge the group's P partials by the log-sum-exp
-// rule.  All threads find the largest running max; wave w then accumulates partials
-// w, w + COMB_WAVES, ... (loads of COMB_UNROLL partials in flight, so that a row's
-// partials take few dependent load rounds), and the waves' sums meet in LDS.
+// One workgroup per (query row (b, h), 32-wide slice of d): merge the group's P partials
+// by the log-sum-exp rule for those 32 output elements.  All threads find the largest
+// running max; each half-wave then accumulates partials hw, hw + 2 COMB_WAVES, ... (lane
+// = element of the slice; loads of COMB_UNROLL partials in flight), and the half-waves'
+// sums meet in LDS.  Spreading a row over D/32 workgroups spreads the partials' bytes
+// over that many CUs.
 template <int D>
 __global__ __launch_bounds__(COMB_WAVES * 64) void decode_combine_kernel(DecArgs a)
 {
-    constexpr int PE = D / 64;
-    __shared__ float red[COMB_WAVES][D + 1];
+    constexpr int SL = D / 32;   // slices per row
+    constexpr int NH = 2 * COMB_WAVES;   // half-waves
+    __shared__ float red[NH][33];
+    __shared__ float wmax[COMB_WAVES];
     const int lane = threadIdx.x & 63, w = wave_id();
-    const int64_t row = blockIdx.x;   // b*Hq + h
+    const int dl = lane & 31, hw = 2 * w + (lane >> 5);
+    const int64_t row = blockIdx.x / SL;   // b*Hq + h
+    const int slice = (int)(blockIdx.x % SL);
     const int h = (int)(row % a.Hq), b = (int)(row / a.Hq);
     const int kv = h / a.G, g = h % a.G;
     const int P = a.nsplit * DEC_NW;
@@ -168,52 +174,43 @@ __global__ __launch_bounds__(COMB_WAVES * 64) void decode_combine_kernel(DecArgs
         M = fmaxf(M, a.part_ml[2 * (first + (int64_t)p * a.G)]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    if (lane == 0) red[w][D] = M;
+    if (lane == 0) wmax[w] = M;
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < COMB_WAVES; ++i) M = fmaxf(M, red[i][D]);
-    __syncthreads();
-    float lsum = 0.f, acc[PE];
-#pragma unroll
-    for (int i = 0; i < PE; ++i) acc[i] = 0.f;
-    for (int p0 = w; p0 < P; p0 += COMB_WAVES * COMB_UNROLL) {
+    for (int i = 0; i < COMB_WAVES; ++i) M = fmaxf(M, wmax[i]);
+    float lsum = 0.f, acc = 0.f;
+    const int e = 32 * slice + dl;   // output element of this lane
+    for (int p0 = hw; p0 < P; p0 += NH * COMB_UNROLL) {
         float2 ml[COMB_UNROLL];
-        float ov[COMB_UNROLL][PE];
+        float ov[COMB_UNROLL];
 #pragma unroll
         for (int u = 0; u < COMB_UNROLL; ++u) {
-            const int p = min(p0 + COMB_WAVES * u, P - 1);
+            const int p = min(p0 + NH * u, P - 1);
             const int64_t pi = first + (int64_t)p * a.G;
             ml[u] = *(const float2*)(a.part_ml + 2 * pi);
-#pragma unroll
-            for (int i = 0; i < PE; ++i) ov[u][i] = a.part_o[pi * D + lane + 64 * i];
+            ov[u] = a.part_o[pi * D + e];
         }
 #pragma unroll
         for (int u = 0; u < COMB_UNROLL; ++u) {
-            if (p0 + COMB_WAVES * u >= P) continue;
+            if (p0 + NH * u >= P) continue;
             const float wgt = fast_exp2((ml[u].x - M) * a.c);   // 0 for an empty partial
             lsum += wgt * ml[u].y;
-#pragma unroll
-            for (int i = 0; i < PE; ++i) acc[i] += wgt * ov[u][i];
+            acc += wgt * ov[u];
         }
     }
-#pragma unroll
-    for (int i = 0; i < PE; ++i) red[w][lane + 64 * i] = acc[i];
-    if (lane == 0) red[w][D] = lsum;
+    red[hw][dl] = acc;
+    if (dl == 0) red[hw][32] = lsum;
     __syncthreads();
-    if (w == 0) {
-        float lt = 0.f;
+    if (threadIdx.x < 32) {
+        float lt = 0.f, v = 0.f;
 #pragma unroll
-        for (int j = 0; j < COMB_WAVES; ++j) lt += red[j][D];
-        const float inv = 1.f / lt;
-#pragma unroll
-        for (int i = 0; i < PE; ++i) {
-            float v = 0.f;
-#pragma unroll
-            for (int j = 0; j < COMB_WAVES; ++j) v += red[j][lane + 64 * i];
-            const __bf16 o = (__bf16)(v * inv);
-            a.O[row * D + lane + 64 * i] = __builtin_bit_cast(uint16_t, o);
+        for (int j = 0; j < NH; ++j) {
+            lt += red[j][32];
+            v += red[j][dl];
         }
-        if (lane == 0) a.lse[row] = a.scale * M + __logf(lt);
+        const __bf16 o = (__bf16)(v / lt);
+        a.O[row * D + e] = __builtin_bit_cast(uint16_t, o);
+        if (slice == 0 && dl == 0) a.lse[row] = a.scale * M + __logf(lt);
     }
 }
 
@@ -274,7 +271,7 @@ hipError_t launch_decode_bf16(const Shape& s, int64_t pos, const void* q, const 
     a.c = s.scale * kLog2e;
     a.scale = s.scale;
     const dim3 grid1((unsigned)(s.B * s.Hk), (unsigned)pl.nsplit);   // nsplit <= 512
-    const unsigned grid2 = (unsigned)(s.B * s.Hq);   // one workgroup per query row
+    const unsigned grid2 = (unsigned)(s.B * s.Hq * (s.d / 32));   // per query row and d-slice
     timing_begin("decode", st);
     if (s.d == 128)
         hipLaunchKernelGGL((decode_partial_kernel<128>), grid1, dim3(DEC_NW * 64), 0, st, a);
