@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_64k")
-    ap.add_argument("--suite", choices=["pages", "decode"], default=None,
+    ap.add_argument("--suite", choices=["pages", "decode", "ablation"], default=None,
                     help="print one JSON line per workload of a measurement suite instead")
     ap.add_argument("--no-aux", action="store_true", help="skip the auxiliary measurements")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -443,6 +443,13 @@ def suite_pages(torch, inputs, steps, warmup):
             fa2, moda, extra = PAGES_A100[name]
             line["pages_a100_context"] = {"fa2_ms": fa2, "moda_ms": moda, "extra_time": extra}
         print(json.dumps(line), flush=True)
+    suite_ablation(torch, inputs)
+
+
+def suite_ablation(torch, inputs):
+    """The kernel ablation of depth-KV layouts at the Table 7 shape (T=1024, G=8, L=64):
+    the forward with each choice of the depth rows a query block scores, one line each,
+    10 launches of each scan in order (scan 0, then 1, then 2; the last 9 timed)."""
     w = inputs.PAGE_WORKLOADS["table7"]
     st = Step(w, w.L, seed=0, pack=False, bwd=False)
     mb, x = st.mb, st.x
@@ -545,13 +552,6 @@ def main():
     from transformer_attention_moda_amd import binding, inputs
     binding.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    if args.suite == "pages":
-        suite_pages(torch, inputs, args.steps, args.warmup)
-        return
-    if args.suite == "decode":
-        suite_decode(torch, inputs, args.steps)
-        return
-    w = inputs.WORKLOADS[args.workload]
     if args.copy_probe_mib > 0:
         # A kernel of known traffic for scaling hardware byte counters: the packer with
         # L = 1 is a plain copy (reads and writes copy_probe_mib MiB once).
@@ -563,6 +563,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
+    if args.suite == "pages":
+        suite_pages(torch, inputs, args.steps, args.warmup)
+        return
+    if args.suite == "decode":
+        suite_decode(torch, inputs, args.steps)
+        return
+    if args.suite == "ablation":
+        suite_ablation(torch, inputs)
+        return
+    w = inputs.WORKLOADS[args.workload]
 
     step = Step(w, w.L, seed=0)
     ms, kernels, wall = step.timed(args.steps, args.warmup)

@@ -4,6 +4,8 @@
     python -m transformer_attention_moda_amd.profile_summary trace <dir> [--by-grid]
     python -m transformer_attention_moda_amd.profile_summary traffic <fetch_dir> <write_dir> \
         <probe_mib> <workload>
+    python -m transformer_attention_moda_amd.profile_summary ablation <fetch_dir> <sq_dir> \
+        <probe_mib>
 
 `counters`: every `*counter_collection.csv` under the given rocprofv3 output
 directories (one per --pmc pass); prints, per libmoda kernel, the mean over its
@@ -23,7 +25,11 @@ resident waves per CU (SQ_WAVE_CYCLES counts in units of 4 cycles).  `traffic`: 
 per launch from a FETCH_SIZE pass and a WRITE_SIZE pass (KiB per dispatch) of
 `bench.py --copy-probe-mib <probe_mib>`, each scaled by what the same counter reads for
 the probe (the packer with L = 1 copying probe_mib MiB: that many bytes read and written),
-in the line format bench.py reads from profiles/traffic.txt.  Nothing here runs on a GPU.
+in the line format bench.py reads from profiles/traffic.txt.  `ablation`: the forward
+dispatches of `bench.py --suite ablation` (the same kernel launched 10 times per depth scan,
+scan 0, 1, 2 in that order) split into their three groups, with per scan the mean duration,
+the HBM bytes fetched (FETCH_SIZE scaled by the copy probe as for `traffic`), the MFMA
+instructions and the fraction of SIMD cycles the matrix cores were busy.  Nothing here runs on a GPU.
 """
 from __future__ import annotations
 
@@ -178,6 +184,43 @@ def trace_by_grid(dirs):
     return "\n".join(out)
 
 
+def ablation(fetch_dir, sq_dir, probe_mib):
+    probe_bytes = probe_mib << 20
+    probe_grid = min((probe_bytes // 16 + 255) // 256, 1 << 20) * 256
+    out = ["scan  launches  mean_us  fetch_GB  mfma_instr  matrix_busy"]
+    per = {}
+    factor = None
+    for d in (fetch_dir, sq_dir):
+        disp = defaultdict(dict)   # dispatch -> counter -> value, plus the duration
+        for r in _rows([d], "counter_collection.csv"):
+            name = r["Kernel_Name"]
+            if "pack_kernel" in name and int(r["Grid_Size"]) == probe_grid and \
+                    r["Counter_Name"] == "FETCH_SIZE" and factor is None:
+                factor = probe_bytes / (float(r["Counter_Value"]) * 1024)
+            if "fwd_bf16_kernel" not in name:
+                continue
+            k = int(r.get("Dispatch_Id") or r.get("Correlation_Id"))
+            disp[k][r["Counter_Name"]] = float(r["Counter_Value"])
+            disp[k]["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+        ids = sorted(disp)
+        n = len(ids) // 3
+        for scan in range(3):
+            group = [disp[i] for i in ids[scan * n:(scan + 1) * n]]
+            for c in group[0]:
+                per.setdefault(scan, {})[c] = sum(g[c] for g in group) / len(group)
+            per[scan]["_n"] = len(group)
+    for scan in range(3):
+        c = per[scan]
+        fetch = c.get("FETCH_SIZE", 0.0) * 1024 * (factor or float("nan")) / 1e9
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (4 * c["SQ_BUSY_CU_CYCLES"]) \
+            if c.get("SQ_BUSY_CU_CYCLES") else float("nan")
+        out.append(f"{scan:4d}  {c['_n']:8d}  {c['_ns'] / 1e3:7.1f}  {fetch:8.3f}  "
+                   f"{c.get('SQ_INSTS_MFMA', float('nan')):10.4g}  {busy:11.3f}")
+    out.append(f"# FETCH_SIZE scale from the copy probe: {factor:.4f}" if factor else
+               "# no copy probe found: fetch_GB not scaled")
+    return "\n".join(out)
+
+
 def trace(dirs):
     out = []
     for r in _rows(dirs, "kernel_stats.csv"):
@@ -190,9 +233,12 @@ def trace(dirs):
 
 
 def main(argv):
-    if len(argv) < 2 or argv[0] not in ("counters", "trace", "traffic"):
+    if len(argv) < 2 or argv[0] not in ("counters", "trace", "traffic", "ablation"):
         print(__doc__)
         return 2
+    if argv[0] == "ablation":
+        print(ablation(argv[1], argv[2], int(argv[3])))
+        return 0
     if argv[0] == "traffic":
         print(traffic(argv[1], argv[2], int(argv[3]), argv[4]))
     else:
