@@ -143,6 +143,14 @@ __device__ __forceinline__ void stage_rows(uint16_t* tile, int nrows, const uint
     }
 }
 
+// An opaque copy of x: the compiler cannot see that it equals x, so the values derived
+// from it are computed where they are used, not kept live (or spilled) from earlier uses.
+__device__ __forceinline__ int opaque(int x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // Index of the calling wave in its workgroup, as a wave-uniform (scalar) value: the
 // compiler cannot prove threadIdx.x / 64 uniform, and every per-wave quantity derived
 // from it would otherwise occupy vector registers.

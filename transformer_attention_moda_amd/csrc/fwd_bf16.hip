@@ -89,6 +89,7 @@ __global__ __launch_bounds__(NW * 64, (D == 64 && NW == 4) ? 3 : 8 / NW) void fw
     static_assert(ELEMS == 2 * 32 * TL::PITCH && (NW == 8 || NW == 4), "depth slices must fit");
 
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int lane_id = lane;
     const int col = lane & 31, hf = lane >> 5;
     const int G = a.G, T = a.T, L = a.L;
 
@@ -149,6 +150,11 @@ __global__ __launch_bounds__(NW * 64, (D == 64 && NW == 4) ? 3 : 8 / NW) void fw
     // slice, its V loads as soon as the current PV has read the V slice.  Mask: virtual
     // row v is visible to token t iff (t - tw_lo)*W <= v < (t - tw_lo)*W + W.
     auto depth_phase = [&]() {
+        // Lane-derived values recomputed here from an opaque copy of the lane index, rather
+        // than kept live (and spilled) across the sequence loop.
+        const int lane = opaque(lane_id);
+        const int hf = lane >> 5;
+        const int tcol = (int)min((fw + (lane & 31)) / G, (int64_t)T - 1);
         const int64_t TL_rows = (int64_t)T * L;
         const uint16_t* Kdb = a.Kd + kvbase * (int64_t)L * D;
         const uint16_t* Vdb = a.Vd + kvbase * (int64_t)L * D;
@@ -362,21 +368,28 @@ __global__ __launch_bounds__(NW * 64, (D == 64 && NW == 4) ? 3 : 8 / NW) void fw
     if (L > 0) depth_phase();
 
     // ---- epilogue ----
-    if (valid) {
-        const float inv = 1.f / l;
-        uint16_t* orow = a.O + (((int64_t)b * a.Hq + hq) * T + tcol) * D;
+    {   // lane-derived values recomputed, as in the depth phase
+        const int lane = opaque(lane_id);
+        const int hf = lane >> 5;
+        const int64_t fcol = fw + (lane & 31);
+        const int tcol = (int)min(fcol / G, (int64_t)T - 1);
+        const int hq = kv * G + (int)(fcol % G);
+        if (fcol < TG) {
+            const float inv = 1.f / l;
+            uint16_t* orow = a.O + (((int64_t)b * a.Hq + hq) * T + tcol) * D;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+            for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                bf16x4 v;
-                v[0] = (__bf16)(o[db][4 * jj + 0] * inv);
-                v[1] = (__bf16)(o[db][4 * jj + 1] * inv);
-                v[2] = (__bf16)(o[db][4 * jj + 2] * inv);
-                v[3] = (__bf16)(o[db][4 * jj + 3] * inv);
-                *(bf16x4*)(orow + 32 * db + 8 * jj + 4 * hf) = v;
-            }
-        if (hf == 0) a.lse[((int64_t)b * a.Hq + hq) * T + tcol] = a.scale * m + __logf(l);
+                for (int jj = 0; jj < 4; ++jj) {
+                    bf16x4 v;
+                    v[0] = (__bf16)(o[db][4 * jj + 0] * inv);
+                    v[1] = (__bf16)(o[db][4 * jj + 1] * inv);
+                    v[2] = (__bf16)(o[db][4 * jj + 2] * inv);
+                    v[3] = (__bf16)(o[db][4 * jj + 3] * inv);
+                    *(bf16x4*)(orow + 32 * db + 8 * jj + 4 * hf) = v;
+                }
+            if (hf == 0) a.lse[((int64_t)b * a.Hq + hq) * T + tcol] = a.scale * m + __logf(l);
+        }
     }
 }
 
