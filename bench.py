@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="long_64k")
+    ap.add_argument("--workload", default="long_64k",
+                    help="a workload of inputs.WORKLOADS or inputs.PAGE_WORKLOADS (default: the 64K one)")
     ap.add_argument("--suite", choices=["pages", "decode", "ablation"], default=None,
                     help="print one JSON line per workload of a measurement suite instead")
     ap.add_argument("--no-aux", action="store_true", help="skip the auxiliary measurements")
@@ -577,7 +578,7 @@ def main():
     if args.suite == "ablation":
         suite_ablation(torch, inputs)
         return
-    w = inputs.WORKLOADS[args.workload]
+    w = inputs.WORKLOADS.get(args.workload) or inputs.PAGE_WORKLOADS[args.workload]
 
     step = Step(w, w.L, seed=0)
     ms, kernels, wall = step.timed(args.steps, args.warmup)
@@ -623,7 +624,9 @@ def main():
     aux = None if args.no_aux else aux_measurements(torch, inputs)
 
     out = {
-        "metric": "MoDA fwd+bwd TFLOP/s bf16 at T=64K (% MFMA peak); overhead vs own L=0 path",
+        "metric": ("MoDA fwd+bwd TFLOP/s bf16 at T=64K (% MFMA peak); overhead vs own L=0 path"
+                   if args.workload == "long_64k" else
+                   f"MoDA fwd+bwd TFLOP/s bf16, {args.workload} (% MFMA peak); overhead vs own L=0 path"),
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
