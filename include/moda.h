@@ -52,7 +52,7 @@ extern "C" {
 typedef enum {
     MODA_OK = 0,
     MODA_ERR_INVALID_ARGUMENT = 1, /* bad shape, pointer, alignment, scale or workspace */
-    MODA_ERR_UNSUPPORTED = 2,      /* valid request outside what this build implements */
+    MODA_ERR_UNSUPPORTED = 2,      /* valid request outside what the library implements */
     MODA_ERR_HIP = 3               /* the HIP runtime reported an error; see moda_last_error */
 } moda_status_t;
 
@@ -61,7 +61,7 @@ typedef enum {
     MODA_F32 = 1   /* fp32 storage and arithmetic throughout */
 } moda_dtype_t;
 
-/* Largest number of depth entries per token this build accepts. */
+/* Largest number of depth entries per token the library accepts. */
 #define MODA_MAX_L 1024
 
 /* moda_problem_t.flags bits. */

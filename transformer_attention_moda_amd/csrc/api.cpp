@@ -82,7 +82,7 @@ moda_status_t check_problem(const moda_problem_t* p, bool need_head_dim, moda::S
     if (32 % G != 0)
         return fail(MODA_ERR_UNSUPPORTED, "GQA group size G = %lld must divide 32", (long long)G);
     if (p->T > kMaxT || p->T * (p->L > 0 ? p->L : 1) > kMaxRows || p->B * p->Hq > kMaxRows / 64)
-        return fail(MODA_ERR_UNSUPPORTED, "sizes beyond this build's 32-bit row indices");
+        return fail(MODA_ERR_UNSUPPORTED, "sizes beyond the kernels' 32-bit row indices");
     // The backward stages a KV group's query rows (G heads of T rows) with 32-bit byte
     // offsets from the tile's first row; they reach (G-1)*T + 64 rows.
     if (((G - 1) * p->T + 64) * p->d * 2 >= (int64_t(1) << 31))
