@@ -148,18 +148,18 @@ class Step:
         return t0.elapsed_time(t1) / steps, kernels, wall
 
 
-def traffic_for(label):
-    """Per-launch HBM traffic of a kernel from the committed rocprofv3 counter
-    summary (profiles/traffic.txt: FETCH_SIZE and WRITE_SIZE, each scaled by
-    the factor a plain copy of known size gives), or None when the kernel's
-    sources changed since those counters were taken."""
+def traffic_for(label, workload):
+    """Per-launch HBM traffic of a kernel at a workload from the committed rocprofv3
+    counter summary (profiles/traffic.txt: FETCH_SIZE and WRITE_SIZE, each scaled by
+    the factor a plain copy of known size gives), or None when that workload was not
+    profiled or the kernel's sources changed since its counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.txt")
     if not os.path.exists(path):
         return None
     for line in open(path):
         f = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
-        if f.get("kernel") != label:
+        if f.get("kernel") != label or f.get("workload") != workload:
             continue
         h = hashlib.sha256()
         for src in f.get("sources", "").split(","):
@@ -608,7 +608,7 @@ def main():
                 "frac": round(ach / peak, 4)}
 
     dom = max(kernels, key=lambda n: kernels[n]["avg_ms"] * kernels[n]["per_step"])
-    roofline = dict(roof(dom, kernels[dom], w), traffic=traffic_for(dom), kernel=dom,
+    roofline = dict(roof(dom, kernels[dom], w), traffic=traffic_for(dom, w.name), kernel=dom,
                     avg_ms=round(kernels[dom]["avg_ms"], 4))
     per_kernel = {n: dict(roof(n, k, w), avg_ms=round(k["avg_ms"], 4),
                           launches_per_step=k["per_step"]) for n, k in kernels.items()}

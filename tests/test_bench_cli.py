@@ -14,3 +14,12 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode != 0
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert line["n_gpus"] == 2 and "one GPU" in line["error"]
+
+
+def test_traffic_is_reported_only_for_the_profiled_workload():
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.traffic_for("bwd_dkdv", "table2_T4096") is None   # never profiled
+    assert bench.traffic_for("no_such_kernel", "long_64k") is None
+    t = bench.traffic_for("bwd_dkdv", "long_64k")   # None once the sources change
+    assert t is None or (t["fetch_bytes"] > 0 and t["bytes"] == t["fetch_bytes"] + t["write_bytes"])
