@@ -414,3 +414,30 @@ def depth_append(packed, layer, L, slot, t0=0, stream=None):
     p = problem(B, Hk, Hk, TL // L, d, L, 1.0, dt)
     moda_depth_append(p, layer, slot, t0, packed, stream)
     return packed
+
+
+class _ModaAttention(torch.autograd.Function):
+    """The operator as one differentiable call: moda_fwd forward, moda_bwd backward."""
+
+    @staticmethod
+    def forward(ctx, Q, K, V, Kd, Vd, L, scale, causal, window):
+        O, lse = fwd(Q, K, V, Kd, Vd, L, scale=scale, causal=causal, window=window)
+        ctx.save_for_backward(Q, K, V, Kd, Vd, O, lse)
+        ctx.cfg = (L, scale, causal, window)
+        return O
+
+    @staticmethod
+    def backward(ctx, dO):
+        Q, K, V, Kd, Vd, O, lse = ctx.saved_tensors
+        L, scale, causal, window = ctx.cfg
+        dQ, dK, dV, dKd, dVd = bwd(Q, K, V, Kd, Vd, O, lse, dO.contiguous(), L, scale=scale,
+                                   causal=causal, window=window)
+        return dQ, dK, dV, dKd, dVd, None, None, None, None
+
+
+def moda_attention(Q, K, V, Kd=None, Vd=None, L=0, scale=None, causal=True, window=0):
+    """O [B,Hq,T,d] of MoDA over Q [B,Hq,T,d], K, V [B,Hk,T,d] and the packed depth rows
+    Kd, Vd [B,Hk,T*L,d] (None when L = 0), differentiable with respect to all five: the
+    backward is moda_bwd.  The interface of the pages' kernel call, with the depth rows
+    already packed (pack_depth) and the scale defaulting to 1/sqrt(d)."""
+    return _ModaAttention.apply(Q, K, V, Kd, Vd, L, scale, causal, window)
