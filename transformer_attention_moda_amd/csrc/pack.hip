@@ -10,11 +10,11 @@
 // ("Mixture-of-Depths Attention", arXiv 2603.15619, paper summary,
 // "Hardware-Efficient Implementation", natural-layout paragraph and
 // "Flash-compatible depth-KV layout").  The kernel is a bitwise copy bound by
-// HBM bandwidth.  Lane i owns 16-byte chunk i of the [B*Hk*T, row] source rows and
-// walks the L layers: for each layer a workgroup reads 256 consecutive chunks (one
-// contiguous span) and writes them as depth row l of their tokens.  Its index
-// division happens once, not per layer; loads and stores are non-temporal (every
-// byte is touched once).
+// HBM bandwidth.  It walks the packed rows in output order, so that a workgroup's
+// stores are one contiguous span (writes are the slower side of a copy on this chip),
+// and reads each 16-byte chunk from its layer: a token's row of one layer is 256
+// contiguous bytes.  Four chunks are in flight per lane, and the grid covers the whole
+// tensor in one pass; loads and stores are non-temporal (every byte is touched once).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -23,27 +23,34 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int PACK_THREADS = 256;
-constexpr int PACK_UNROLL = 8;   // layers in flight per lane
+constexpr int PACK_UNROLL = 4;   // chunks in flight per lane
 
 __global__ __launch_bounds__(PACK_THREADS) void pack_kernel(const u32x4* __restrict__ in,
                                                             u32x4* __restrict__ out, int L,
                                                             int64_t chunks, int64_t cpr)
 {
-    // chunks = B*Hk*T*cpr source chunks per layer; chunk i is chunk i % cpr of row i / cpr.
-    for (int64_t i = (int64_t)blockIdx.x * PACK_THREADS + threadIdx.x; i < chunks;
-         i += (int64_t)gridDim.x * PACK_THREADS) {
-        const int64_t row = i / cpr, ch = i - row * cpr;
-        const u32x4* src = in + i;
-        u32x4* dst = out + row * L * cpr + ch;
-        int l = 0;
-        for (; l + PACK_UNROLL <= L; l += PACK_UNROLL) {
-            u32x4 v[PACK_UNROLL];
+    // chunks = B*Hk*T*cpr source chunks per layer.  Packed chunk j, of packed row
+    // pr = ((b*Hk + kv)*T + t)*L + l, is chunk (pr / L)*cpr + j % cpr of layer pr % L.
+    const int64_t total = (int64_t)L * chunks;
+    const int64_t stride = (int64_t)gridDim.x * PACK_THREADS * PACK_UNROLL;
+    for (int64_t base = (int64_t)blockIdx.x * PACK_THREADS * PACK_UNROLL + threadIdx.x;
+         base < total; base += stride) {
+        u32x4 v[PACK_UNROLL];
 #pragma unroll
-            for (int u = 0; u < PACK_UNROLL; ++u) v[u] = __builtin_nontemporal_load(src + (l + u) * chunks);
-#pragma unroll
-            for (int u = 0; u < PACK_UNROLL; ++u) __builtin_nontemporal_store(v[u], dst + (l + u) * cpr);
+        for (int u = 0; u < PACK_UNROLL; ++u) {
+            const int64_t j = base + u * PACK_THREADS;
+            if (j < total) {
+                const int64_t pr = j / cpr, ch = j - pr * cpr;
+                const int64_t bt = pr / L;
+                const int l = (int)(pr - bt * L);
+                v[u] = __builtin_nontemporal_load(in + l * chunks + bt * cpr + ch);
+            }
         }
-        for (; l < L; ++l) __builtin_nontemporal_store(__builtin_nontemporal_load(src + l * chunks), dst + l * cpr);
+#pragma unroll
+        for (int u = 0; u < PACK_UNROLL; ++u) {
+            const int64_t j = base + u * PACK_THREADS;
+            if (j < total) __builtin_nontemporal_store(v[u], out + j);
+        }
     }
 }
 
@@ -86,7 +93,7 @@ hipError_t launch_pack_depth(int64_t L, int64_t B, int64_t Hk, int64_t T, int64_
 {
     const int64_t cpr = row_bytes / 16;
     const int64_t chunks = B * Hk * T * cpr;
-    int64_t blocks = (chunks + PACK_THREADS - 1) / PACK_THREADS;
+    int64_t blocks = (L * chunks + PACK_THREADS * PACK_UNROLL - 1) / (PACK_THREADS * PACK_UNROLL);
     if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;
     timing_begin("pack", st);
     hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(PACK_THREADS), 0, st,
