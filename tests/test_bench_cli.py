@@ -23,3 +23,19 @@ def test_traffic_is_reported_only_for_the_profiled_workload():
     assert bench.traffic_for("no_such_kernel", "long_64k") is None
     t = bench.traffic_for("bwd_dkdv", "long_64k")   # None once the sources change
     assert t is None or (t["fetch_bytes"] > 0 and t["bytes"] == t["fetch_bytes"] + t["write_bytes"])
+
+
+def test_copy_probe_grid_follows_the_packer_launch():
+    """The traffic summary finds bench.py's copy probe by the packer's grid; the launch
+    constants are read from the packer's source so that a change there fails here."""
+    import re
+    sys.path.insert(0, ROOT)
+    from transformer_attention_moda_amd import profile_summary
+    src = open(os.path.join(ROOT, "transformer_attention_moda_amd", "csrc", "pack.hip")).read()
+    threads = int(re.search(r"PACK_THREADS\s*=\s*(\d+)", src).group(1))
+    unroll = int(re.search(r"PACK_UNROLL\s*=\s*(\d+)", src).group(1))
+    cap = 1 << int(re.search(r"blocks\s*>\s*\(int64_t\(1\)\s*<<\s*(\d+)\)", src).group(1))
+    for mib in (1, 1024, 3072, 1 << 16):
+        chunks = (mib << 20) // 16
+        blocks = min(-(-chunks // (threads * unroll)), cap)
+        assert profile_summary.packer_grid(mib << 20) == blocks * threads

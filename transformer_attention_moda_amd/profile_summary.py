@@ -2,6 +2,7 @@
 
     python -m transformer_attention_moda_amd.profile_summary counters <dir> [<dir> ...]
     python -m transformer_attention_moda_amd.profile_summary trace <dir> [--by-grid]
+    python -m transformer_attention_moda_amd.profile_summary dispatches <dir> <kernel>
     python -m transformer_attention_moda_amd.profile_summary traffic <fetch_dir> <write_dir> \
         <probe_mib> <workload>
     python -m transformer_attention_moda_amd.profile_summary ablation <fetch_dir> <sq_dir> \
@@ -13,7 +14,9 @@ dispatches of each counter, the dispatch count and the mean duration, then the
 derived rates below.  `trace`: every `*kernel_stats.csv` (rocprofv3
 --kernel-trace --stats), the per-kernel call count and mean duration; with --by-grid, from
 `*kernel_trace.csv`, the count and median duration per kernel and launch grid (one line per
-problem size when a run launches a kernel at several).
+problem size when a run launches a kernel at several).  `dispatches`: from
+`*kernel_trace.csv`, every dispatch of the kernels whose name contains <kernel>, in launch
+order, with its grid and duration.
 
 Derived (when the counters are present): GRBM_GUI_ACTIVE / duration = the
 graphics clock the counter ran at (summed over the chip's XCDs, so divided by
@@ -128,10 +131,16 @@ def sources_sha(label):
     return h.hexdigest()[:16]
 
 
+def packer_grid(nbytes):
+    """Work-items of the packer's launch for a copy of nbytes with L = 1: 256-lane
+    workgroups of 4 16-byte chunks per lane, at most 2^20 workgroups."""
+    chunks = nbytes // 16
+    return min((chunks + 1023) // 1024, 1 << 20) * 256
+
+
 def traffic(fetch_dir, write_dir, probe_mib, workload):
     probe_bytes = probe_mib << 20
-    chunks = probe_bytes // 16
-    probe_grid = min((chunks + 255) // 256, 1 << 20) * 256   # the packer's launch
+    probe_grid = packer_grid(probe_bytes)
     per = {}
     factors = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -186,7 +195,7 @@ def trace_by_grid(dirs):
 
 def ablation(fetch_dir, sq_dir, probe_mib):
     probe_bytes = probe_mib << 20
-    probe_grid = min((probe_bytes // 16 + 255) // 256, 1 << 20) * 256
+    probe_grid = packer_grid(probe_bytes)
     out = ["scan  launches  mean_us  fetch_GB  mfma_instr  matrix_busy"]
     per = {}
     factor = None
@@ -221,6 +230,17 @@ def ablation(fetch_dir, sq_dir, probe_mib):
     return "\n".join(out)
 
 
+def dispatches(dirs, kernel):
+    rows = [r for r in _rows(dirs, "kernel_trace.csv") if kernel in r.get("Kernel_Name", "")]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    out = []
+    for i, r in enumerate(rows):
+        grid = "x".join(r[f"Grid_Size_{a}"] for a in "XYZ")
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        out.append(f"{i:3d} {short_name(r['Kernel_Name']):44s} grid={grid:18s} us={us:10.1f}")
+    return "\n".join(out)
+
+
 def trace(dirs):
     out = []
     for r in _rows(dirs, "kernel_stats.csv"):
@@ -233,7 +253,7 @@ def trace(dirs):
 
 
 def main(argv):
-    if len(argv) < 2 or argv[0] not in ("counters", "trace", "traffic", "ablation"):
+    if len(argv) < 2 or argv[0] not in ("counters", "trace", "traffic", "ablation", "dispatches"):
         print(__doc__)
         return 2
     if argv[0] == "ablation":
@@ -241,6 +261,8 @@ def main(argv):
         return 0
     if argv[0] == "traffic":
         print(traffic(argv[1], argv[2], int(argv[3]), argv[4]))
+    elif argv[0] == "dispatches":
+        print(dispatches([argv[1]], argv[2]))
     else:
         if argv[0] == "counters":
             print(counters(argv[1:]))
