@@ -55,6 +55,9 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-l0", action="store_true", help="skip the L=0 comparison run")
+    ap.add_argument("--no-same-cache", action="store_true",
+                    help="decode suite: skip the back-to-back calls on one cache (so that a "
+                         "kernel trace holds only calls that cycle through the caches)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain copy of this many MiB first through the packer with "
                          "L=1 (a kernel of known traffic for scaling hardware byte counters)")
@@ -483,56 +486,93 @@ def suite_ablation(torch, inputs):
 LOOP_CALLS = 20
 
 
-def suite_decode(torch, inputs, steps):
+def suite_decode(torch, inputs, steps, same_cache=True):
     """Decode, depth append and the variants at the 64K shape (B=1, Hq=16, Hk=8, d=128,
     L=24), each against its roofline."""
     from transformer_attention_moda_amd import binding as mb
     w = inputs.WORKLOADS["long_64k"]
+    # A decoding loop calls the operator once per layer, each call on that layer's own cache.
+    # The timed calls therefore cycle through several K/V caches, at least 1 GiB in all, so
+    # that none is still in the 256 MB last-level cache when its turn comes round again. The
+    # time of back-to-back calls on one cache, which that cache partly serves, is reported
+    # beside it.
     for B, window in ((1, 0), (16, 0), (1, 4)):
         wb = w.with_(B=B)
         x = inputs.make(wb, seed=0, device="cuda:0", names=("Q", "K", "V", "Kd", "Vd"))
+        kv_bytes = 2 * 2 * B * w.Hk * w.T * w.d
+        ncache = max(2, -(-(1 << 30) // kv_bytes))
+        caches = [(x["K"], x["V"])] + [
+            tuple(inputs.make(wb, seed=i, device="cuda:0", names=("K", "V")).values())
+            for i in range(1, ncache)]
         q = x["Q"][:, :, -1].contiguous()
         p = mb.problem(B, w.Hq, w.Hk, w.T, w.d, w.L, w.scale, window=window)
         O = torch.empty_like(q)
         lse = torch.empty((B, w.Hq), device="cuda:0")
         ws = torch.empty(mb.moda_decode_workspace_bytes(p), device="cuda:0", dtype=torch.uint8)
-        run = lambda: mb.moda_decode(p, w.T - 1, q, x["K"], x["V"], x["Kd"], x["Vd"], O, lse, ws)  # noqa: E731
-        run()
-        ms_one = events_ms(torch, run, max(steps, 9))
-        ms = events_ms(torch, lambda: [run() for _ in range(LOOP_CALLS)], 9) / LOOP_CALLS
-        # One call captured in a HIP graph and replayed: no host-side work per step.
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            run()
-        ms_graph = events_ms(torch, graph.replay, max(steps, 9))
-        del graph
+        calls = [lambda K=K, V=V: mb.moda_decode(p, w.T - 1, q, K, V, x["Kd"], x["Vd"], O, lse, ws)
+                 for K, V in caches]
+        turn = [0]
+
+        def next_call():
+            calls[turn[0] % ncache]()
+            turn[0] += 1
+        for c in calls:
+            c()
+        ms_one = events_ms(torch, next_call, max(steps, 9))
+        ms = events_ms(torch, lambda: [next_call() for _ in range(LOOP_CALLS)], 9) / LOOP_CALLS
+        ms_same = (events_ms(torch, lambda: [calls[0]() for _ in range(LOOP_CALLS)], 9) / LOOP_CALLS
+                   if same_cache else None)
+        # One call per cache captured in a HIP graph and replayed in turn: no host-side work.
+        graphs = []
+        for c in calls:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                c()
+            graphs.append(g)
+        gturn = [0]
+
+        def next_replay():
+            graphs[gturn[0] % ncache].replay()
+            gturn[0] += 1
+        ms_graph = events_ms(torch, next_replay, max(steps, 9))
+        del graphs
         W = window or w.L
         nbytes = 2 * (2 * B * w.Hk * w.T * w.d + 2 * B * w.Hk * W * w.d + 2 * B * w.Hq * w.d)
         print(json.dumps({
             "metric": "MoDA decode step GB/s (one new token, 64K cache)",
             "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
             "config": {"workload": "decode_64k", "B": B, "Hq": w.Hq, "Hk": w.Hk, "T": w.T,
-                       "d": w.d, "L": w.L, "window": window},
+                       "d": w.d, "L": w.L, "window": window, "caches_in_turn": ncache},
             "us": round(ms * 1e3, 2), "us_single_call": round(ms_one * 1e3, 2),
-            "us_graph_replay": round(ms_graph * 1e3, 2), "bytes": nbytes,
+            "us_graph_replay": round(ms_graph * 1e3, 2),
+            "us_same_cache": round(ms_same * 1e3, 2) if ms_same else None, "bytes": nbytes,
             "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
-        del x, q, O, lse, ws
+        del x, caches, calls, q, O, lse, ws
         torch.cuda.empty_cache()
-    layer = inputs.normal((w.B, w.Hk, w.T, w.d), seed=0, tensor="layers_K", device="cuda:0")
+    # The append, likewise, takes its layers in turn, each into its own slot.
+    nlay = 4
+    layers = [inputs.normal((w.B, w.Hk, w.T, w.d), seed=i, tensor="layers_K", device="cuda:0")
+              for i in range(nlay)]
     packed = torch.empty((w.B, w.Hk, w.T * w.L, w.d), device="cuda:0", dtype=torch.bfloat16)
     p = mb.problem(w.B, w.Hk, w.Hk, w.T, w.d, w.L, 1.0)
-    run = lambda: mb.moda_depth_append(p, layer, 5, 0, packed)  # noqa: E731
-    run()
-    ms_one = events_ms(torch, run, 9)
-    ms = events_ms(torch, lambda: [run() for _ in range(LOOP_CALLS)], 9) / LOOP_CALLS
-    nbytes = 2 * layer.numel() * 2
+    aturn = [0]
+
+    def next_append():
+        i = aturn[0] % nlay
+        mb.moda_depth_append(p, layers[i], i, 0, packed)
+        aturn[0] += 1
+    for _ in range(nlay):
+        next_append()
+    ms_one = events_ms(torch, next_append, 9)
+    ms = events_ms(torch, lambda: [next_append() for _ in range(LOOP_CALLS)], 9) / LOOP_CALLS
+    nbytes = 2 * layers[0].numel() * 2
     print(json.dumps({"metric": "MoDA depth-cache append GB/s (one layer, 64K tokens)",
                       "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
                       "config": {"workload": "append_64k", "B": w.B, "Hk": w.Hk, "T": w.T,
-                                 "d": w.d, "L": w.L},
+                                 "d": w.d, "L": w.L, "layers_in_turn": nlay},
                       "us": round(ms * 1e3, 2), "us_single_call": round(ms_one * 1e3, 2),
                       "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
-    del layer, packed
+    del layers, packed
     torch.cuda.empty_cache()
     st = Step(w, w.L, seed=0, pack=False, causal=False)
     ms, k, _ = st.timed(max(3, steps // 3), 1)
@@ -580,7 +620,7 @@ def main():
         suite_pages(torch, inputs, args.steps, args.warmup)
         return
     if args.suite == "decode":
-        suite_decode(torch, inputs, args.steps)
+        suite_decode(torch, inputs, args.steps, same_cache=not args.no_same_cache)
         return
     if args.suite == "ablation":
         suite_ablation(torch, inputs)

@@ -10,8 +10,9 @@
 // The work is one long, thin reduction, bound by the bytes of K and V it
 // streams (4 d bytes per key, each used by the G heads of its group), so it is
 // split over the sequence: for each (b, kv) the visible keys, then the depth
-// rows, form 32-row blocks; every wave of every workgroup takes a contiguous
-// run of blocks and keeps an online-softmax partial (running max m, sum l,
+// rows, form 32-row blocks; with P waves on the (b, kv), wave p takes blocks
+// p, p + P, p + 2P, ... (so that the waves of a unit read neighbouring blocks
+// at about the same time) and keeps an online-softmax partial (running max m, sum l,
 // unnormalised output o) for the G query heads of the group, held in the 32
 // MFMA columns (columns past G repeat heads; their results are not written).
 // Per block: S^T = K q^T on 32x32x16 bf16 MFMA with K rows loaded straight
@@ -42,7 +43,6 @@ struct DecArgs {
     int pos;              // the query's token position in the cache
     int nseq;             // visible sequence keys 0..nseq-1
     int nblk_seq, nblk;   // 32-row blocks: the sequence ones first, then the depth ones
-    int bpw;              // blocks per wave
     int nsplit;           // workgroups per (b, kv)
     float c;              // scale * log2(e)
     float scale;
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(DEC_NW * 64) void decode_partial_kernel(DecArgs a)
     const int bkv = blockIdx.x, kv = bkv % a.Hk, b = bkv / a.Hk;
     const int G = a.G, P = a.nsplit * DEC_NW;
     const int part = blockIdx.y * DEC_NW + w;
-    const int blk0 = part * a.bpw, blk1 = min(blk0 + a.bpw, a.nblk);
+    const int nblk = a.nblk;   // this wave's blocks: part, part + P, ... below nblk
 
     bf16x8 qreg[D / 16];   // q^T columns as MFMA B operands, k-step si: d = 16 si + 8 hf ..
     {
@@ -103,12 +103,12 @@ __global__ __launch_bounds__(DEC_NW * 64) void decode_partial_kernel(DecArgs a)
         block_src(i, kb, vb, count);
         stage_rows<D>(slot, 32, vb, [&](int r) { return min(r, count - 1) * D; }, lane, 0, 1);
     };
-    if (blk0 < blk1) {
-        issue_v(blk0);
-        issue_k(blk0);
+    if (part < nblk) {
+        issue_v(part);
+        issue_k(part);
     }
-    for (int i = blk0; i < blk1; ++i) {
-        const bool more = i + 1 < blk1;
+    for (int i = part; i < nblk; i += P) {
+        const bool more = i + P < nblk;
         const uint16_t *kb, *vb;
         int count;
         block_src(i, kb, vb, count);
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(DEC_NW * 64) void decode_partial_kernel(DecArgs a)
         for (int j = 0; j < 16; ++j) s[0][j] = 0.f;
 #pragma unroll
         for (int si = 0; si < D / 16; ++si) s[0] = mfma32(kr[si], qreg[si], s[0]);
-        if (more) issue_k(i + 1);
+        if (more) issue_k(i + P);
         // register j holds row (j/4)*8 + 4 hf + j%4 of the block
 #pragma unroll
         for (int j = 0; j < 16; ++j)
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(DEC_NW * 64) void decode_partial_kernel(DecArgs a)
         wave_lds_sync();
         pv_block<D>(slot, 0, s[0], o, lane);
         wave_lds_sync();
-        if (more) issue_v(i + 1);
+        if (more) issue_v(i + P);
     }
 
     // The partial of query head kv*G + col (columns past G repeat heads: not written).
@@ -222,11 +222,13 @@ DecodePlan plan_decode(const Shape& s, int64_t nseq)
     const int64_t units = s.B * s.Hk;
     pl.nblk_seq = (nseq + 31) / 32;
     pl.nblk = pl.nblk_seq + (s.L > 0 ? (s.W + 31) / 32 : 0);
-    // About 2048 waves over the chip (8 per CU), at least 2 blocks per wave; the split
-    // count never decreases as nseq grows, so the largest nseq bounds the workspace.
-    const int64_t cap = std::max<int64_t>(1, 2048 / (DEC_NW * units));
+    // At d = 128 one wave per SIMD holds the partial kernel's registers, so one 4-wave
+    // workgroup per CU: about 1024 waves over the chip's 256 CUs, in a single round. At
+    // d = 64 three waves fit per SIMD, and about 2048 waves are launched. At least 2 blocks
+    // per wave. The split count never decreases as nseq grows, so the largest nseq bounds
+    // the workspace.
+    const int64_t cap = std::max<int64_t>(1, (s.d == 128 ? 1024 : 2048) / (DEC_NW * units));
     pl.nsplit = std::min<int64_t>(cap, (pl.nblk + 2 * DEC_NW - 1) / (2 * DEC_NW));
-    pl.bpw = (pl.nblk + DEC_NW * pl.nsplit - 1) / (DEC_NW * pl.nsplit);
     const int64_t parts = units * pl.nsplit * DEC_NW * s.G;
     pl.o_floats = parts * s.d;
     pl.ml_floats = parts * 2;
@@ -266,7 +268,6 @@ hipError_t launch_decode_bf16(const Shape& s, int64_t pos, const void* q, const 
     a.nseq = (int)nseq;
     a.nblk_seq = (int)pl.nblk_seq;
     a.nblk = (int)pl.nblk;
-    a.bpw = (int)pl.bpw;
     a.nsplit = (int)pl.nsplit;
     a.c = s.scale * kLog2e;
     a.scale = s.scale;

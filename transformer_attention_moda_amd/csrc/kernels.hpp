@@ -56,7 +56,7 @@ hipError_t launch_bwd_f32(const Shape& s, const float* Q, const float* K, const 
 // partials, and the launch.  nseq: visible sequence keys.
 struct DecodePlan {
     int64_t nblk_seq, nblk;   // 32-row blocks: sequence, then depth
-    int64_t nsplit, bpw;      // workgroups per (b, kv); blocks per wave
+    int64_t nsplit;           // workgroups per (b, kv)
     int64_t o_floats, ml_floats;
 };
 DecodePlan plan_decode(const Shape& s, int64_t nseq);
