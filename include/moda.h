@@ -31,9 +31,16 @@
  * Ownership and execution.  All tensors are device memory owned by the
  * caller.  The library never allocates, frees or synchronises device memory;
  * each call validates its arguments on the host, enqueues its kernels on
- * `stream` (a hipStream_t; NULL means the null stream) and returns.  Device
- * faults surface at the caller's next synchronisation.  Outputs must not alias
- * inputs or each other.  Pointers must be 16-byte aligned.
+ * `stream` (a hipStream_t; NULL means the null stream) and returns.  One
+ * exception to "on `stream`": moda_bwd on a small problem runs one of its
+ * kernels on a second stream of the current device, forked from `stream` by
+ * an event and joined back into it by another, so work enqueued on `stream`
+ * after the call is ordered after all of it, as if it had run on `stream`.
+ * That stream and its two events are created by the first such call on a
+ * device (not while `stream` is being captured into a graph) and kept until
+ * the process ends.  Device faults surface at the caller's next
+ * synchronisation.  Outputs must not alias inputs or each other.  Pointers
+ * must be 16-byte aligned.
  *
  * Errors.  Every argument check runs before anything is launched; on a
  * non-OK status nothing was enqueued and outputs are untouched.

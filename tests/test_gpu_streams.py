@@ -1,7 +1,9 @@
 """GPU: libmoda runs on the caller's stream and allocates and synchronises nothing,
-so its calls work on a side stream and inside a captured HIP graph.  Results are
-compared bitwise with the same calls made eagerly on the default stream (the
-kernels are deterministic)."""
+so its calls work on a side stream and inside a captured HIP graph.  (On small problems
+the backward's key pass runs on a second stream of the library's, forked from the
+caller's stream by an event and joined back into it by another: work the caller enqueues
+after the call still sees every gradient.)  Results are compared bitwise with the same
+calls made eagerly on the default stream (the kernels are deterministic)."""
 import pytest
 import torch
 
@@ -55,6 +57,28 @@ def test_calls_run_on_the_callers_side_stream(shape):
     s.synchronize()
     for k in NAMES:
         assert torch.equal(o[k], ref[k]), k
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_work_enqueued_after_the_backward_sees_its_gradients(shape):
+    """The key pass's dK and dV, written on the library's second stream, are complete for a
+    copy the caller enqueues on its own stream right after the call, with no synchronisation
+    between them."""
+    p, x, o = _setup(shape=shape)
+    _run(p, x, o)
+    torch.cuda.synchronize()
+    ref = {k: o[k].clone() for k in NAMES}
+    s = torch.cuda.Stream()
+    for rep in range(3):
+        for k in NAMES:
+            o[k].fill_(float("nan"))
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            _run(p, x, o)
+            copies = {k: o[k].clone() for k in NAMES}
+        s.synchronize()
+        for k in NAMES:
+            assert torch.equal(copies[k], ref[k]), (rep, k)
 
 
 @pytest.mark.parametrize("shape", SHAPES)

@@ -220,12 +220,12 @@ moda_status_t check_bwd(const moda_problem_t* p, const void* Q, const void* K, c
 moda_status_t launch_bwd(const moda_problem_t* p, const moda::Shape& s, const void* Q,
                          const void* K, const void* V, const void* Kd, const void* Vd,
                          const void* O, const float* lse, const void* dO, void* dQ, void* dK,
-                         void* dV, void* dKd, void* dVd, void* ws, hipStream_t hs)
+                         void* dV, void* dKd, void* dVd, void* ws, hipStream_t hs, bool side)
 {
     hipError_t e;
     if (p->dtype == MODA_BF16)
         e = moda::launch_bwd_bf16(s, Q, K, V, Kd, Vd, O, lse, dO, dQ, dK, dV, dKd, dVd,
-                                  (float*)ws, hs);
+                                  (float*)ws, hs, side);
     else
         e = moda::launch_bwd_f32(s, (const float*)Q, (const float*)K, (const float*)V,
                                  (const float*)Kd, (const float*)Vd, (const float*)O, lse,
@@ -365,7 +365,7 @@ moda_status_t moda_bwd(const moda_problem_t* p, const void* Q, const void* K, co
         return fail(MODA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu required",
                     workspace_bytes, need);
     return launch_bwd(p, s, Q, K, V, Kd, Vd, O, lse, dO, dQ, dK, dV, dKd, dVd, workspace,
-                      reinterpret_cast<hipStream_t>(stream));
+                      reinterpret_cast<hipStream_t>(stream), true);
 }
 
 moda_status_t moda_bwd_noalloc(const moda_problem_t* p, const void* Q, const void* K,
@@ -386,7 +386,8 @@ moda_status_t moda_bwd_noalloc(const moda_problem_t* p, const void* Q, const voi
     if ((st = device_scratch(hs, &ws)) != MODA_OK) return st;
     // The kernels write every scratch value they read (per-row lse and D first, then
     // the depth part of dQ), so nothing needs clearing between calls.
-    return launch_bwd(p, s, Q, K, V, Kd, Vd, O, lse, dO, dQ, dK, dV, dKd, dVd, ws, hs);
+    // Every launch stays on the caller's stream: no stream or event is created here.
+    return launch_bwd(p, s, Q, K, V, Kd, Vd, O, lse, dO, dQ, dK, dV, dKd, dVd, ws, hs, false);
 }
 
 size_t moda_decode_workspace_bytes(const moda_problem_t* p)

@@ -9,7 +9,8 @@
 //   dK  = scale sum over queries of dS Q,      dV  = sum over queries of p dO
 //   dKd = scale sum over the token's G heads of dS Q, dVd = same with p dO
 //
-// Four kernels, in this order, none with atomics (results are deterministic):
+// Four kernels, none with atomics (results are deterministic); bwd_dkdv depends only
+// on bwd_pre, the other two run in this order:
 //   bwd_pre    D and lse in log2 units, one per query row (workspace);
 //   bwd_depth  per wave, its tokens' depth rows: S_d = Q Kd^T (lane = depth
 //              row), dVd^T += dO^T P_d, dKd^T += Q^T dS_d, and the depth part of
@@ -23,12 +24,20 @@
 //              S = Q K^T, dP = dO V^T (lane = key), dV^T += dO^T P and
 //              dK^T += Q^T dS with dO and Q read transposed from LDS.
 //
+// Streams.  On small problems (at most 1024 key workgroups of 4 waves) the key-stationary
+// pass runs on a second stream of the device, forked from the caller's stream after
+// bwd_pre by an event and joined back into it by another, so that it shares the chip with
+// bwd_depth and bwd_dq: each kernel's last, partly idle stretch is filled by the other.
+// On larger grids the tails are a small part of the time and the two kernels on one chip
+// slow each other, so they run one after the other on the caller's stream.
+//
 // Variants.  Non-causal (runtime flag): every key is visible to every query, so
 // bwd_dq walks all key tiles and bwd_dkdv all query rows, masking only ragged
 // ends.  A depth window (the last W of L slots): bwd_depth gives the hidden
 // slots weight 0, so their dKd, dVd rows are written as exact zeros and they add
 // nothing to dQ.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -761,18 +770,46 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void bwd_depth_kernel(Bwd
     }
 }
 
+// The second stream of the current device and the two events that fork it from and join
+// it to the caller's stream, created on first use and kept until the process ends.  Not
+// created while the caller's stream is being captured into a graph (the pass then stays
+// on that stream) or when the caller's stream belongs to another device.
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    bool tried = false;
+};
+constexpr int kSideDevices = 64;
+std::mutex g_side_mutex;   // guards the table and each fork ... join sequence
+SideStream g_side[kSideDevices];
+
+SideStream* side_stream(hipStream_t st)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSideDevices) return nullptr;
+    if (st) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(st, &sdev) != hipSuccess || sdev != dev) return nullptr;
+    }
+    SideStream& ss = g_side[dev];
+    if (!ss.tried) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+            return nullptr;
+        ss.tried = true;
+        if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
+            hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+            ss.stream = nullptr;
+    }
+    return ss.stream ? &ss : nullptr;
+}
+
 template <int D>
-hipError_t run(const Shape& s, BwdArgs a, hipStream_t st)
+void launch_depth_dq(const Shape& s, BwdArgs a, hipStream_t st)
 {
     const int nunits = (int)(s.B * s.Hk);
     const int64_t TG = s.T * s.G;
-    {
-        constexpr int RPB = 256 / (D / 8);
-        timing_begin("bwd_pre", st);
-        hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((a.rows + RPB - 1) / RPB)),
-                           dim3(256), 0, st, a);
-        timing_end(st);
-    }
     if (s.L > 0) {
         constexpr int NW = 4;
         a.nblocks = (int)((TG + NW * 32 - 1) / (NW * 32));
@@ -790,36 +827,74 @@ hipError_t run(const Shape& s, BwdArgs a, hipStream_t st)
                            dim3(NW * 64), 0, st, a);
         timing_end(st);
     }
-    {
-        constexpr int NW = 4;
-        const DkdvPlan pl = plan_dkdv(s);
-        a.nkeyblocks = pl.key_blocks;
-        a.piece_tiles = pl.piece_tiles;
-        a.nblocks = pl.pieces_per_unit;
-        const unsigned grid = (unsigned)(nunits * a.nblocks);
-        timing_begin("bwd_dkdv", st);
-        bool two = false;
-        if constexpr (D == 64) two = grid >= 1024;   // four workgroups per CU or more
-        if (two) {
-            // One 8-wave workgroup of 256 keys per CU (two waves per SIMD): each staged
-            // query tile serves 8 waves rather than 4 (2-8% faster than two 4-wave ones).
-            constexpr int NW2 = 8;
-            a.nblocks = (int)((s.T + NW2 * 32 - 1) / (NW2 * 32));
-            hipLaunchKernelGGL((bwd_dkdv_kernel<64, NW2, 2, false>), dim3((unsigned)(nunits * a.nblocks)),
-                               dim3(NW2 * 64), 0, st, a);
-        }
-        else if (pl.piece_tiles > 0)
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, 1, true>), dim3(grid), dim3(NW * 64), 0, st, a);
-        else
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, 1, false>), dim3(grid), dim3(NW * 64), 0, st, a);
+}
+
+// d = 64 grids of 1024 key workgroups or more: one 8-wave workgroup of 256 keys per CU
+// (two waves per SIMD), so that each staged query tile serves 8 waves rather than 4 (2-8%
+// faster than two 4-wave ones).
+template <int D>
+bool dkdv_two_waves(const Shape& s, const DkdvPlan& pl)
+{
+    return D == 64 && s.B * s.Hk * pl.pieces_per_unit >= 1024;
+}
+
+template <int D>
+void launch_dkdv(const Shape& s, BwdArgs a, const DkdvPlan& pl, hipStream_t st)
+{
+    constexpr int NW = 4;
+    const int nunits = (int)(s.B * s.Hk);
+    a.nkeyblocks = pl.key_blocks;
+    a.piece_tiles = pl.piece_tiles;
+    a.nblocks = pl.pieces_per_unit;
+    const unsigned grid = (unsigned)(nunits * a.nblocks);
+    timing_begin("bwd_dkdv", st);
+    if (dkdv_two_waves<D>(s, pl)) {
+        constexpr int NW2 = 8;
+        a.nblocks = (int)((s.T + NW2 * 32 - 1) / (NW2 * 32));
+        hipLaunchKernelGGL((bwd_dkdv_kernel<64, NW2, 2, false>), dim3((unsigned)(nunits * a.nblocks)),
+                           dim3(NW2 * 64), 0, st, a);
+    }
+    else if (pl.piece_tiles > 0)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, 1, true>), dim3(grid), dim3(NW * 64), 0, st, a);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, 1, false>), dim3(grid), dim3(NW * 64), 0, st, a);
+    timing_end(st);
+    if (pl.piece_tiles > 0) {
+        timing_begin("dkdv_reduce", st);
+        hipLaunchKernelGGL((dkdv_reduce_kernel<D>), dim3((unsigned)(nunits * pl.key_blocks)),
+                           dim3(256), 0, st, a);
         timing_end(st);
-        if (pl.piece_tiles > 0) {
-            timing_begin("dkdv_reduce", st);
-            hipLaunchKernelGGL((dkdv_reduce_kernel<D>), dim3((unsigned)(nunits * pl.key_blocks)),
-                               dim3(256), 0, st, a);
-            timing_end(st);
+    }
+}
+
+template <int D>
+hipError_t run(const Shape& s, BwdArgs a, hipStream_t st, bool side)
+{
+    {
+        constexpr int RPB = 256 / (D / 8);
+        timing_begin("bwd_pre", st);
+        hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((a.rows + RPB - 1) / RPB)),
+                           dim3(256), 0, st, a);
+        timing_end(st);
+    }
+    const DkdvPlan pl = plan_dkdv(s);
+    side = side && !dkdv_two_waves<D>(s, pl) && s.B * s.Hk * pl.key_blocks <= 1024;
+    if (side) {
+        std::lock_guard<std::mutex> guard(g_side_mutex);
+        if (SideStream* ss = side_stream(st)) {
+            hipError_t e = hipEventRecord(ss->fork, st);
+            if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->fork, 0);
+            if (e != hipSuccess) return e;
+            launch_depth_dq<D>(s, a, st);
+            launch_dkdv<D>(s, a, pl, ss->stream);
+            e = hipEventRecord(ss->join, ss->stream);
+            if (e == hipSuccess) e = hipStreamWaitEvent(st, ss->join, 0);
+            if (e != hipSuccess) return e;
+            return hipGetLastError();
         }
     }
+    launch_depth_dq<D>(s, a, st);
+    launch_dkdv<D>(s, a, pl, st);
     return hipGetLastError();
 }
 
@@ -855,7 +930,7 @@ DkdvPlan plan_dkdv(const Shape& s)
 hipError_t launch_bwd_bf16(const Shape& s, const void* Q, const void* K, const void* V,
                            const void* Kd, const void* Vd, const void* O, const float* lse,
                            const void* dO, void* dQ, void* dK, void* dV, void* dKd, void* dVd,
-                           float* ws, hipStream_t st)
+                           float* ws, hipStream_t st, bool side)
 {
     BwdArgs a;
     a.Q = (const uint16_t*)Q;
@@ -890,7 +965,7 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* Q, const void* K, const v
     a.nblocks = 1;
     a.piece_tiles = 0;
     a.nkeyblocks = 0;
-    return s.d == 128 ? run<128>(s, a, st) : run<64>(s, a, st);
+    return s.d == 128 ? run<128>(s, a, st, side) : run<64>(s, a, st, side);
 }
 
 }  // namespace moda

@@ -39,10 +39,12 @@ DkdvPlan plan_dkdv(const Shape& s);
 
 // Backward, bfloat16 storage.  ws: the workspace (lse2 and D per row, the depth part of
 // dQ when L > 0, then the split pass's partials; sizes as the ABI's workspace query).
+// side: small problems may run the key-stationary pass on the device's second stream,
+// forked from and joined back into st (false keeps every launch on st).
 hipError_t launch_bwd_bf16(const Shape& s, const void* Q, const void* K, const void* V,
                            const void* Kd, const void* Vd, const void* O, const float* lse,
                            const void* dO, void* dQ, void* dK, void* dV, void* dKd, void* dVd,
-                           float* ws, hipStream_t st);
+                           float* ws, hipStream_t st, bool side);
 
 // fp32 forward / backward (plain wave-per-row kernels).
 hipError_t launch_fwd_f32(const Shape& s, const float* Q, const float* K, const float* V,
