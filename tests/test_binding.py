@@ -106,3 +106,16 @@ def test_pack_depth_shapes_are_checked():
                            torch.zeros(B, Hk, T * L, d, dtype=BF))
     with pytest.raises(ValueError, match="layers"):
         mb.pack_depth(torch.zeros(B, Hk, T, d, dtype=BF))
+
+
+def test_depth_kv_cache_shapes_and_host_append():
+    """DepthKVCache holds the packed [B,Hk,T*L,d] pair; empty sizes are refused, and an append
+    into host tensors is refused before any launch."""
+    with pytest.raises(ValueError):
+        mb.DepthKVCache(B, Hk, T, 0, d, device="cpu")
+    c = mb.DepthKVCache(B, Hk, T, L, d, device="cpu")
+    Kd, Vd = c.tensors()
+    assert Kd.shape == (B, Hk, T * L, d) and Vd.shape == Kd.shape and Kd.dtype == BF
+    layer = torch.zeros(B, Hk, T, d, dtype=BF)
+    with pytest.raises(ValueError, match="GPU"):
+        c.append(layer, layer, 0)

@@ -145,3 +145,26 @@ def test_append_then_decode_round_trip():
     decode_check(w, q, x, T - 1, tag=" appended cache")
     torch.cuda.synchronize()
     assert torch.equal(Kd.view(torch.int16), binding.pack_depth(layers["layers_K"]).view(torch.int16))
+
+
+def test_depth_kv_cache_class_fills_the_packed_layout():
+    """DepthKVCache filled one layer per slot holds exactly the packer's output for K and V,
+    and the operator reads it as it reads packed tensors (bitwise equal O)."""
+    L, B, Hq, Hk, T, d = 5, 1, 4, 2, 70, 128
+    lk = inputs.normal((L, B, Hk, T, d), seed=31, tensor="layers_K", device=DEV)
+    lv = inputs.normal((L, B, Hk, T, d), seed=31, tensor="layers_V", device=DEV)
+    c = binding.DepthKVCache(B, Hk, T, L, d, device=DEV)
+    for l in range(L):
+        c.append(lk[l].contiguous(), lv[l].contiguous(), l)
+    Kd, Vd = c.tensors()
+    pk, pv = binding.pack_depth(lk), binding.pack_depth(lv)
+    torch.cuda.synchronize()
+    assert torch.equal(Kd.view(torch.int16), pk.view(torch.int16))
+    assert torch.equal(Vd.view(torch.int16), pv.view(torch.int16))
+    q = inputs.normal((B, Hq, T, d), seed=32, tensor="Q", device=DEV)
+    k = inputs.normal((B, Hk, T, d), seed=32, tensor="K", device=DEV)
+    v = inputs.normal((B, Hk, T, d), seed=32, tensor="V", device=DEV)
+    O1 = binding.moda_attention(q, k, v, Kd, Vd, L)
+    O2, _ = binding.fwd(q, k, v, pk, pv, L)
+    torch.cuda.synchronize()
+    assert torch.equal(O1.view(torch.int16), O2.view(torch.int16))

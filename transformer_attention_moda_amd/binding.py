@@ -416,6 +416,33 @@ def depth_append(packed, layer, L, slot, t0=0, stream=None):
     return packed
 
 
+class DepthKVCache:
+    """The depth rows of L slots per token for one attention call, as the packed pair
+    Kd, Vd [B,Hk,T*L,d] (token-major: row t*L + slot) that moda_fwd, moda_bwd and
+    moda_decode read, filled one layer at a time by moda_depth_append.  This is the role the
+    moda-attention 0.1.0 PyPI page ("Architecture") gives its DepthKVCache: contiguous depth
+    KV storage across layers.  The tensors start as zeros; a caller writes every slot it lets
+    the operator see before calling it."""
+
+    def __init__(self, B, Hk, T, L, d, dtype=torch.bfloat16, device="cuda"):
+        if min(B, Hk, T, L, d) < 1:
+            raise ValueError(f"B, Hk, T, L and d must be >= 1; got {(B, Hk, T, L, d)}")
+        self.L = int(L)
+        self.K = torch.zeros((B, Hk, T * L, d), dtype=dtype, device=device)
+        self.V = torch.zeros_like(self.K)
+
+    def append(self, k_layer, v_layer, slot, t0=0, stream=None):
+        """Write one layer's K and V rows [B,Hk,n,d] of tokens t0..t0+n-1 into depth slot
+        `slot` of both tensors."""
+        depth_append(self.K, k_layer, self.L, slot, t0, stream)
+        depth_append(self.V, v_layer, self.L, slot, t0, stream)
+        return self
+
+    def tensors(self):
+        """(Kd, Vd): the packed depth rows to pass to the operator with this L."""
+        return self.K, self.V
+
+
 class _ModaAttention(torch.autograd.Function):
     """The operator as one differentiable call: moda_fwd forward, moda_bwd backward."""
 
