@@ -18,7 +18,10 @@ utilisation of the tiling.
 `--suite pages` prints one JSON line per kernel workload of the pages' efficiency
 tables (sequence, group and depth sweeps at d=64) and per depth-scan ablation
 mode; `--suite decode` one line each for the decoding step, the depth-cache
-append and the non-causal and windowed variants at the 64K shape.
+append and the non-causal and windowed variants at the 64K shape; `--suite
+ceiling` one line per setting of the matrix-core rate probe (libmoda_probe.so):
+the chip's sustained bf16 MFMA rate and clock with no memory traffic, the
+context for the attention kernels' fractions of the nominal peak.
 """
 from __future__ import annotations
 
@@ -48,7 +51,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_64k",
                     help="a workload of inputs.WORKLOADS or inputs.PAGE_WORKLOADS (default: the 64K one)")
-    ap.add_argument("--suite", choices=["pages", "decode", "ablation"], default=None,
+    ap.add_argument("--suite", choices=["pages", "decode", "ablation", "ceiling"], default=None,
                     help="print one JSON line per workload of a measurement suite instead")
     ap.add_argument("--no-aux", action="store_true", help="skip the auxiliary measurements")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -486,6 +489,58 @@ def suite_ablation(torch, inputs):
 LOOP_CALLS = 20
 
 
+def suite_ceiling(torch, launch_ms=20.0, timed=10):
+    """The chip's sustained bf16 matrix-core rate: the probe kernel of libmoda_probe.so (four
+    independent 32x32x16 MFMA chains per wave, no memory traffic in its loop) on every CU, at
+    one and two waves per SIMD, with fixed B operands (a loop of MFMAs and loop control only)
+    and with one operand register changed after each MFMA (one vector instruction each).  Each setting runs
+    3 untimed launches, then `timed` launches of about launch_ms each back to back; the line
+    gives their median rate and the mean shader clock (s_memtime ticks over 100 MHz
+    s_memrealtime ticks of each workgroup)."""
+    import ctypes
+    import statistics
+    lib = ctypes.CDLL(os.path.join(ROOT, "transformer_attention_moda_amd", "libmoda_probe.so"))
+    lib.moda_probe_mfma.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.moda_probe_mfma.restype = ctypes.c_int
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream().cuda_stream
+    flop_per_iter_wave = 4 * 32768                       # four MFMAs of 32x32x16
+    for wps in (1, 2):
+        wg = ncu * wps
+        # Iterations for about launch_ms at the nominal peak.
+        iters = int(launch_ms * 1e-3 * MFMA_BF16_PEAK_TFLOPS * 1e12
+                    / (wg * 4 * flop_per_iter_wave)) // 4 * 4   # the probe unrolls by 4
+        sink = torch.empty(wg * 256, device="cuda:0", dtype=torch.float32)
+        clocks = torch.zeros(2 * wg, device="cuda:0", dtype=torch.int64)
+        for vary in (0, 1):
+            def launch():
+                rc = lib.moda_probe_mfma(wg, iters, wps, vary, sink.data_ptr(), clocks.data_ptr(),
+                                         stream)
+                if rc != 0:
+                    raise RuntimeError(f"moda_probe_mfma failed ({rc})")
+            for _ in range(3):
+                launch()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(timed + 1)]
+            ev[0].record()
+            for i in range(timed):
+                launch()
+                ev[i + 1].record()
+            torch.cuda.synchronize()
+            c = clocks.view(wg, 2).double()
+            ghz = float((c[:, 0] / c[:, 1]).mean()) * 0.1   # the last launch's clock
+            ms = statistics.median(ev[i].elapsed_time(ev[i + 1]) for i in range(timed))
+            tf = wg * 4 * iters * flop_per_iter_wave / (ms * 1e-3) / 1e12
+            print(json.dumps({
+                "metric": "sustained bf16 MFMA rate (probe, no memory traffic)",
+                "value": round(tf, 1), "unit": "TFLOP/s",
+                "frac_nominal": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                "clock_GHz": round(ghz, 3), "waves_per_simd": wps,
+                "operands": "changing" if vary else "fixed", "ms_per_launch": round(ms, 3),
+                "launches": timed, "cus": ncu}), flush=True)
+        del sink, clocks
+
+
 def suite_decode(torch, inputs, steps, same_cache=True):
     """Decode, depth append and the variants at the 64K shape (B=1, Hq=16, Hk=8, d=128,
     L=24), each against its roofline."""
@@ -624,6 +679,9 @@ def main():
         return
     if args.suite == "ablation":
         suite_ablation(torch, inputs)
+        return
+    if args.suite == "ceiling":
+        suite_ceiling(torch)
         return
     w = inputs.WORKLOADS.get(args.workload) or inputs.PAGE_WORKLOADS[args.workload]
 

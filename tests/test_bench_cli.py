@@ -39,3 +39,21 @@ def test_copy_probe_grid_follows_the_packer_launch():
         chunks = (mib << 20) // 16
         blocks = min(-(-chunks // (threads * unroll)), cap)
         assert profile_summary.packer_grid(mib << 20) == blocks * threads
+
+
+def test_mfma_probe_library_refuses_bad_arguments_on_the_host():
+    """The ceiling suite's probe library is built beside libmoda.so and checks its arguments
+    before any launch (no GPU call is made for a refused one)."""
+    import ctypes
+    path = os.path.join(ROOT, "transformer_attention_moda_amd", "libmoda_probe.so")
+    assert os.path.exists(path), "run __graft_entry__.build() first"
+    lib = ctypes.CDLL(path)
+    f = lib.moda_probe_mfma
+    f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    buf = ctypes.c_void_p(256)   # never dereferenced: every call below is refused first
+    assert f(0, 10, 1, 0, buf, buf, None) != 0        # no workgroups
+    assert f(256, 3, 1, 0, buf, buf, None) != 0       # fewer iterations than one unrolled round
+    assert f(256, 10, 3, 0, buf, buf, None) != 0      # waves per SIMD must be 1 or 2
+    assert f(256, 10, 1, 0, None, buf, None) != 0     # null output

@@ -15,6 +15,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoda.so")
+# The matrix-core rate probe (bench.py --suite ceiling): a library of its own, outside the
+# operator's C ABI.
+PROBE_SRC = "probe_mfma.hip"
+PROBE_LIB = os.path.join(HERE, "libmoda_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "decode.hip", "rowwise.hip", "pack.hip"]
@@ -38,11 +42,13 @@ def _compile(src: str) -> str:
 
 def build() -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
+        objs = list(ex.map(_compile, SOURCES + [PROBE_SRC]))
+    for lib, lib_objs in ((LIB, objs[:-1]), (PROBE_LIB, objs[-1:])):
+        tmp = lib + ".tmp"
+        subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
+                               *lib_objs])
+        os.replace(tmp, lib)
     return LIB
 
 

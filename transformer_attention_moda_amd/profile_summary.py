@@ -47,6 +47,11 @@ XCDS = 8            # MI355X: 8 accelerator complex dies ...
 CUS_PER_XCD = 32    # ... of 32 compute units each
 
 
+def ours(kernel: str) -> bool:
+    """A kernel of libmoda (namespace moda) or of its matrix-core rate probe."""
+    return "moda" in kernel or "mfma_probe_kernel" in kernel
+
+
 def short_name(kernel: str) -> str:
     """`void moda::(anonymous namespace)::fwd_bf16_kernel<128, 8, false>(...)` ->
     `fwd_bf16_kernel<128, 8, false>`."""
@@ -67,7 +72,7 @@ def counters(dirs):
     dur = defaultdict(dict)                           # kernel -> dispatch -> ns
     for r in _rows(dirs, "counter_collection.csv"):
         name = r.get("Kernel_Name", "")
-        if "moda" not in name:
+        if not ours(name):
             continue
         k = short_name(name)
         key = (r.get("Dispatch_Id") or r.get("Correlation_Id"), r.get("Counter_Name"))
@@ -147,7 +152,7 @@ def traffic(fetch_dir, write_dir, probe_mib, workload):
         vals = defaultdict(list)
         probe = None
         for r in _rows([d], "counter_collection.csv"):
-            if r["Counter_Name"] != counter or "moda" not in r["Kernel_Name"]:
+            if r["Counter_Name"] != counter or not ours(r["Kernel_Name"]):
                 continue
             k = LABELS.get(short_name(r["Kernel_Name"]).split("<")[0])
             if k == "pack" and int(r["Grid_Size"]) == probe_grid and probe is None:
@@ -180,7 +185,7 @@ def traffic(fetch_dir, write_dir, probe_mib, workload):
 def trace_by_grid(dirs):
     durs = defaultdict(list)
     for r in _rows(dirs, "kernel_trace.csv"):
-        if "moda" not in r.get("Kernel_Name", ""):
+        if not ours(r.get("Kernel_Name", "")):
             continue
         grid = "x".join(r[f"Grid_Size_{a}"] for a in "XYZ")
         durs[(short_name(r["Kernel_Name"]), grid)].append(
@@ -244,7 +249,7 @@ def dispatches(dirs, kernel):
 def trace(dirs):
     out = []
     for r in _rows(dirs, "kernel_stats.csv"):
-        if "moda" not in r.get("Name", ""):
+        if not ours(r.get("Name", "")):
             continue
         out.append(f"{short_name(r['Name']):44s} calls={r['Calls']:>5s} "
                    f"mean_us={float(r['AverageNs']) / 1e3:10.1f} "
